@@ -1,0 +1,190 @@
+"""CPU oracle for the FP8 block-scaled NT GEMM and its two M-grouped MoE variants.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, the smoke check in __graft_entry__.py and the
+CPU-baseline leg of bench.py may import or run this module; the library never does.
+It shares no code, table or helper with the HIP path.
+
+What it computes (DeepGEMM pages: FP8 GEMM with DeepSeek-V3 fine-grained scaling and
+two-level "promotion" accumulation -- es.news.hada.io/topic?id=19444 intro bullets;
+bquan.live post 9429818, "Comprender profundamente DeepGEMM"; NT layout with BF16
+output -- same post, "¿Cómo usarlo?"; es.news.hada.io/topic?id=19459 "Interfaz GEMM y
+restricciones de layout"):
+
+    D[m, n] = bf16_rne( sum_kb  P_kb[m, n] * sa[kb, m] * sb[n // 128, kb] )
+    P_kb[m, n] = sum_{k in block kb} e4m3(A[m, k]) * e4m3(B[n, k])
+
+with one FP32 scale per row per 128-wide K block for A (sa, stored K-block-major
+[K/128, ld_sa]) and one FP32 scale per 128x128 block for B (sb [ceil(N/128), K/128]).
+The pages name the scheme but not the block sizes; 1x128 / 128x128 is the DeepSeek-V3
+granularity they refer to.
+
+Precision: every block partial P_kb is computed in FP64 and is EXACT in any summation
+order -- a decoded e4m3 value times 2^9 is an integer below 2^18, so a product times
+2^18 is an integer below 2^36 and a 128-term sum stays below 2^43 < 2^53. The scaled
+sum over blocks is FP64 (one rounding per operation), then a single round-to-nearest-
+even to BF16.
+
+Grouped variants ("Dense y Grouped GEMM", es.news.hada.io/topic?id=19459):
+  contiguous -- rows of all experts concatenated along M; row r uses expert
+                m_indices[r]; rows with -1 are padding and keep their old output.
+  masked     -- A is [G, M_max, K]; only the first masked_m[g] rows of group g are
+                computed, the rest keep their old output.
+
+Every function below is pinned by tests/test_oracle_*.py (brute force in exact
+rationals, bit-exact integer cases, a closed-form scale-indexing probe, library
+cross-checks and invariants).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+
+
+# ------------------------------------------------------------------ e4m3 decode
+def _e4m3_value(code: int) -> float:
+    """OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+    S.1111.111 is NaN; exponent field 0 is subnormal (2^-6 * m/8); max 448."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """uint8 e4m3 codes -> exact float64 values."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# ------------------------------------------------------------------ bf16 rounding
+def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest, ties to even) -> uint16 bits.
+
+    A single rounding straight from float64. bfloat16 keeps 8 significant bits and
+    the float32 exponent range: for |x| in [2^(e-1), 2^e) the spacing is 2^(e-8),
+    and below 2^-126 (subnormal) the spacing is fixed at 2^-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    nan = np.isnan(x)
+    _, e = np.frexp(x)
+    spacing_exp = np.maximum(e, -125) - 8
+    q = np.rint(np.ldexp(x, -spacing_exp))          # np.rint: round half to even
+    v = np.ldexp(q, spacing_exp)
+    with np.errstate(over="ignore"):
+        f32 = v.astype(np.float32)                  # exact: <= 8 significant bits
+    bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    # values that rounded past the largest finite bfloat16 become infinity
+    big = np.abs(v) >= 2.0 ** 128
+    bits = np.where(big, np.where(x < 0, 0xFF80, 0x7F80), bits).astype(np.uint16)
+    out[...] = bits
+    out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ core sum
+def scaled_block_sum(A: np.ndarray, sa: np.ndarray, B: np.ndarray, sb: np.ndarray,
+                     rows=None, cols=None) -> np.ndarray:
+    """S[m, n] = sum_kb P_kb[m, n] * sa[kb, m] * sb[n // 128, kb] in float64.
+
+    A uint8 [M, K], sa float32 [K/128, >=M], B uint8 [N, K], sb float32
+    [ceil(N/128), K/128]. ``rows`` / ``cols`` select a subset of outputs (index
+    arrays into M and N); the result is [len(rows), len(cols)].
+    """
+    A = np.asarray(A, dtype=np.uint8)
+    B = np.asarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and K % BLOCK == 0
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+    sa = np.asarray(sa, dtype=np.float32)
+    sb = np.asarray(sb, dtype=np.float32)
+    Ar = A[rows]
+    Bc = B[cols]
+    S = np.zeros((len(rows), len(cols)), dtype=np.float64)   # starts at +0.0
+    for kb in range(K // BLOCK):
+        a = decode_e4m3(Ar[:, kb * BLOCK:(kb + 1) * BLOCK])
+        b = decode_e4m3(Bc[:, kb * BLOCK:(kb + 1) * BLOCK])
+        P = a @ b.T                                   # exact block partial
+        s = sa[kb, rows].astype(np.float64)[:, None] * sb[cols // BLOCK, kb].astype(np.float64)[None, :]
+        S += P * s                                    # promotion with both scales
+    return S
+
+
+# ------------------------------------------------------------------ the three calls
+def gemm_nt(A, sa, B, sb):
+    """Dense D = A B^T. Returns (bf16 bits uint16 [M, N], float64 S [M, N])."""
+    S = scaled_block_sum(A, sa, B, sb)
+    return bf16_bits_rne(S), S
+
+
+def gemm_nt_sampled(A, sa, B, sb, rows, cols):
+    """Dense D restricted to the outputs rows x cols: (bits, S) of shape [len(rows), len(cols)]."""
+    S = scaled_block_sum(A, sa, B, sb, rows, cols)
+    return bf16_bits_rne(S), S
+
+
+def grouped_contiguous(A, sa, B, sb, m_indices, D_in, rows=None, cols=None):
+    """M-grouped contiguous GEMM.
+
+    A uint8 [M_total, K]; sa [K/128, >=M_total]; B uint8 [G, N, K];
+    sb [G, ceil(N/128), K/128]; m_indices int32 [M_total] (-1 = padding row);
+    D_in uint16 bits [M_total, N] (the output buffer before the call).
+    Returns (D_out bits [len(rows), len(cols)], S float64 with NaN on padding rows).
+    ``rows`` / ``cols`` restrict the computation to a sample.
+    """
+    m_indices = np.asarray(m_indices, dtype=np.int64)
+    Mt = A.shape[0]
+    N = B.shape[1]
+    rows = np.arange(Mt) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+    D = np.array(np.asarray(D_in, dtype=np.uint16)[np.ix_(rows, cols)], copy=True)
+    S = np.full((len(rows), len(cols)), np.nan)
+    for g in np.unique(m_indices[rows]):
+        if g < 0:
+            continue
+        sel = np.nonzero(m_indices[rows] == g)[0]
+        Sg = scaled_block_sum(A, sa, B[g], sb[g], rows[sel], cols)
+        S[sel] = Sg
+        D[sel] = bf16_bits_rne(Sg)
+    return D, S
+
+
+def grouped_masked(A, sa, B, sb, masked_m, D_in, rows=None, cols=None):
+    """M-grouped masked GEMM.
+
+    A uint8 [G, M_max, K]; sa [G, K/128, >=M_max]; B uint8 [G, N, K];
+    sb [G, ceil(N/128), K/128]; masked_m int [G]; D_in bits [G, M_max, N].
+    Rows m >= masked_m[g] keep D_in. Returns (D_out bits, S with NaN on dead rows),
+    optionally restricted to rows/cols within each group.
+    """
+    G, M_max, _ = A.shape
+    N = B.shape[1]
+    rows = np.arange(M_max) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+    D = np.array(np.asarray(D_in, dtype=np.uint16)[:, rows][:, :, cols], copy=True)
+    S = np.full((G, len(rows), len(cols)), np.nan)
+    for g in range(G):
+        live = int(masked_m[g])
+        sel = np.nonzero(rows < live)[0]
+        if len(sel) == 0:
+            continue
+        Sg = scaled_block_sum(A[g], sa[g], B[g], sb[g], rows[sel], cols)
+        S[g, sel] = Sg
+        D[g, sel] = bf16_bits_rne(Sg)
+    return D, S
