@@ -1,0 +1,197 @@
+"""Benchmark of the FP8 block-scaled NT GEMM on one MI355X.
+
+One step = one pass over the dense DeepSeek-V3-like shape list (M in {64, 128, 4096}
+x (N, K) in {(2112,7168), (24576,1536), (32768,512), (7168,16384), (4096,7168),
+(7168,2048)}), A ~ N(0,1) and B ~ N(0,0.02) quantised to e4m3 with 1x128 / 128x128
+FP32 scales, BF16 output. Every shape has its own resident operands (no operand is
+reused within a step, so each GEMM streams its inputs from HBM). Prints one JSON line.
+
+  value     = total algorithmic FP8 FLOPs of a step / measured step time (TFLOP/s)
+  per_shape = per-GEMM kernel time from HIP events on the launch stream, FP8 TFLOP/s,
+              HBM GB/s of the algorithmic bytes, and the fraction of the binding roofline
+  roofline  = the same for the shape that takes the most time
+  cpu_baseline = the CPU oracle timed on one full shape on this host
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "FP8 TFLOPS & GB/s per shape, 1×MI355X, % of FP8 MFMA peak / HBM roofline"
+CONFIG2 = [(m, n, k) for m in (64, 128, 4096)
+           for (n, k) in ((2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048))]
+
+
+def algo_work(M, N, K, G=1):
+    """Algorithmic FLOPs and HBM bytes of one dense call (each operand read once, D written once)."""
+    flops = 2.0 * M * N * K
+    kb = K // 128
+    nbytes = M * K + G * N * K + M * N * 2 + M * kb * 4 + G * ((N + 127) // 128) * kb * 4
+    return flops, nbytes
+
+
+def classify(flops, nbytes):
+    t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    return ("mfma", t_mfma) if t_mfma >= t_hbm else ("hbm", t_hbm)
+
+
+def parse_shapes(text):
+    out = []
+    for item in text.split(";"):
+        m, n, k = (int(x) for x in item.split(","))
+        out.append((m, n, k))
+    return out
+
+
+def cpu_baseline():
+    """The CPU oracle (as it stands) on the full M=4096, N=4096, K=7168 dense shape."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = None
+    M, N, K = 4096, 4096, 7168
+    c = synth.dense_case(M, N, K, seed=99, device="cpu")
+    args = [c[k].numpy() for k in ("A", "sa", "B", "sb")]
+    t0 = time.perf_counter()
+    oracle.gemm_nt(*args)
+    dt = time.perf_counter() - t0
+    threads = None
+    if threadpool_info is not None:
+        info = threadpool_info()
+        blas = [i for i in info if i.get("user_api") == "blas"]
+        if blas:
+            threads = int(blas[0].get("num_threads"))
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    del torch
+    return {"value": round(2.0 * M * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "full oracle (e4m3 decode, per-128-K FP64 block matmul, scaling, BF16 RNE) of the "
+                      "dense M=4096 N=4096 K=7168 shape, 240 GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_config2.json"))
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported" % args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_fp32_amd as fg
+    import synth
+
+    dev = torch.device("cuda:0")
+    shapes = parse_shapes(args.shapes) if args.shapes else CONFIG2
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02)
+        c["ws"] = fg.make_workspace(fg.KIND_DENSE, M, N, K, device=dev)
+        c["cfg"] = fg.query_config(fg.KIND_DENSE, M, N, K)
+        cases.append(c)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, c in enumerate(cases):
+            if events is not None:
+                events[i][0].record()
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: whole steps (value / ms_per_step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # timed region 2: per-kernel durations with events on the launch stream
+    per = [[0.0] for _ in cases]
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
+        step(ev)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            per[i][0] += a.elapsed_time(b)
+    traffic = {}
+    if os.path.exists(args.traffic_file):
+        with open(args.traffic_file) as f:
+            traffic = json.load(f)
+
+    total_flops = 0.0
+    rows = []
+    for i, ((M, N, K), c) in enumerate(zip(shapes, cases)):
+        flops, nbytes = algo_work(M, N, K)
+        total_flops += flops
+        ms = per[i][0] / args.steps
+        bound, t_ideal = classify(flops, nbytes)
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        frac = (tflops / PEAK_FP8_TFLOPS) if bound == "mfma" else (gbs / PEAK_HBM_GBS)
+        rows.append({"M": M, "N": N, "K": K, "us": round(ms * 1e3, 2), "tflops": round(tflops, 1),
+                     "gbs": round(gbs, 1), "bound": bound, "frac": round(frac, 4),
+                     "ideal_us": round(t_ideal * 1e6, 2), "tile": "%dx%d" % (c["cfg"]["block_m"], c["cfg"]["block_n"]),
+                     "split_k": c["cfg"]["split_k"], "algo_bytes": nbytes, "algo_flops": flops})
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(rows, key=lambda r: r["us"])
+    key = "%d,%d,%d" % (dom["M"], dom["N"], dom["K"])
+    tr = traffic.get(key)
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / PEAK_FP8_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = tr["bytes_per_launch"] if tr else None
+    roof["kernel"] = "fp8_gemm_kernel M=%d N=%d K=%d tile %s split %d" % (
+        dom["M"], dom["N"], dom["K"], dom["tile"], dom["split_k"])
+    roof["avg_us"] = dom["us"]
+    roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense FP8 NT GEMM with 1x128/128x128 FP32 scales and BF16 output over %d "
+                               "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)" % len(shapes),
+                   "shapes": ["%dx%dx%d" % s for s in shapes]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_shape": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * fp8gemm.h -- C ABI of libfp8gemm.so: FP8 (e4m3) NT GEMM with fine-grained FP32
+ * block scaling and BF16 output, dense and M-grouped (MoE), for AMD MI355X (gfx950).
+ *
+ * Operation (all three entry points):
+ *
+ *     D[m, n] = bf16( sum_kb  P_kb[m, n] * sa[kb][m] * sb[n / 128][kb] )
+ *     P_kb[m, n] = sum_{k = 128 kb}^{128 kb + 127}  A[m, k] * B[n, k]
+ *
+ * i.e. D = A . B^T ("NT": A row-major [M, K], B row-major [N, K] = B^T column-major),
+ * with each 128-wide K block's partial product promoted into an FP32 accumulator
+ * after multiplying it by the activation scale sa (one per row per 128 K) and the
+ * weight scale sb (one per 128x128 block). Sources: DeepGEMM pages --
+ * es.news.hada.io/topic?id=19444 (intro: FP8 GEMM with DeepSeek-V3 fine-grained
+ * scaling; two-level "promotion" accumulation), bquan.live post 9429818
+ * ("¿Cómo usarlo?": NT format, BF16 output, dense / contiguous / masked entry
+ * points), es.news.hada.io/topic?id=19459 ("Interfaz GEMM y restricciones de
+ * layout": NT only, LHS scales transposed and FP32; "Dense y Grouped GEMM":
+ * M-grouped contiguous and masked layouts), deepep.org/zh/deepgemm (接口设计).
+ * The pages name the scaling scheme but not its block sizes; 1x128 (A) and
+ * 128x128 (B) are the DeepSeek-V3 granularity they refer to.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates, frees or synchronises, and never reads device memory from the host.
+ *  - Work is enqueued on `stream` (NULL = the default stream); buffers must stay
+ *    valid until that work completes. Calls are asynchronous.
+ *  - e4m3 = OCP E4M3FN bytes (max 448; 0x7F/0xFF are NaN). bf16 = uint16 bits.
+ *  - Strides are in ELEMENTS of the pointed-to type. K % 128 == 0.
+ *    lda, ldb >= K and multiples of 16; ldd >= N; ld_sa >= the number of rows it
+ *    covers and a multiple of 4; A, B 16-byte aligned, D 2-byte aligned (8-byte
+ *    aligned with ldd % 4 == 0 for the fast 8-byte store path), sa / sb 4-byte
+ *    aligned.
+ *  - Rounding: FP32 accumulation, one round-to-nearest-even to BF16 per output.
+ *  - Return value: FP8GEMM_OK (0) or a negative FP8GEMM_ERR_* code. On an
+ *    argument error nothing is launched. No exception crosses the ABI.
+ *  - Preconditions on device data (cannot be checked from the host): no e4m3 NaN
+ *    codes in live rows; m_indices / masked_m as documented per call.
+ *  - Split-K workspace: optional. When `workspace` is NULL or smaller than
+ *    fp8_gemm_workspace_size(...), the call runs without split-K. A workspace must
+ *    be zero-filled before its first use; every call leaves it zeroed again (its
+ *    counters self-reset). Calls that run concurrently must not share a workspace.
+ */
+#ifndef FP8GEMM_H_
+#define FP8GEMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FP8GEMM_OK = 0,
+  FP8GEMM_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  FP8GEMM_ERR_SHAPE = -2,     /* M, N, K, G <= 0 (M may be 0 where noted), K % 128   */
+  FP8GEMM_ERR_LAYOUT = -3,    /* stride / leading dimension / alignment violated     */
+  FP8GEMM_ERR_WORKSPACE = -4, /* forced split-K config needs more workspace          */
+  FP8GEMM_ERR_DEVICE = -5,    /* current device is not gfx950 / cannot be queried    */
+  FP8GEMM_ERR_LAUNCH = -6,    /* the HIP launch reported an error                    */
+  FP8GEMM_ERR_CONFIG = -7     /* an invalid forced tile configuration                */
+};
+
+enum { FP8GEMM_KIND_DENSE = 0, FP8GEMM_KIND_CONTIGUOUS = 1, FP8GEMM_KIND_MASKED = 2 };
+
+/* Tile configuration chosen for (or forced on) a call. */
+typedef struct {
+  int block_m;    /* output rows per work unit                                   */
+  int block_n;    /* output columns per work unit                                */
+  int split_k;    /* K splits per output tile (1 = none; > 1 uses the workspace) */
+  int grid;       /* workgroups launched (persistent loop over work units)       */
+  int num_units;  /* work units (tiles x splits); an upper bound for masked      */
+} fp8gemm_config_t;
+
+/*
+ * Dense D[M, N] = A[M, K] . B[N, K]^T.
+ *   A  e4m3 [M, K] row-major, row stride lda.
+ *   sa fp32 [K/128][ld_sa]: sa[kb * ld_sa + m] scales row m of K block kb
+ *      (the transposed, M-contiguous layout), ld_sa >= M.
+ *   B  e4m3 [N, K] row-major, row stride ldb.
+ *   sb fp32 [ceil(N/128)][K/128]: sb[(n/128) * (K/128) + kb]; a last partial block
+ *      of columns (N % 128 != 0) has its own scale row.
+ *   D  bf16 [M, N] row-major, row stride ldd; fully overwritten. M == 0 is a no-op.
+ */
+int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                const void* B, int64_t ldb, const float* sb,
+                void* D, int64_t ldd, int M, int N, int K,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * M-grouped contiguous GEMM (MoE training forward / inference prefill; pages:
+ * es.news.hada.io/topic?id=19459 "Dense y Grouped GEMM", contiguous layout).
+ * The tokens of all G experts are concatenated along M; each expert segment is
+ * padded to a multiple of fp8_gemm_get_mk_alignment_for_contiguous_layout() (128)
+ * rows, and N and K are shared by all experts.
+ *   A  e4m3 [M_total, K] (stride lda); sa fp32 [K/128][ld_sa], ld_sa >= M_total.
+ *   B  e4m3 [G, N, K]: expert g at B + g * N * ldb; sb fp32 [G][ceil(N/128)][K/128].
+ *   D  bf16 [M_total, N] (stride ldd).
+ *   m_indices int32 [M_total] on the device: expert of row r, or -1 for a padding
+ *      row. Precondition: within every 128-row block all entries other than -1
+ *      are equal and < G. Rows with -1 are not written (D keeps its contents).
+ *      Blocks made only of -1 rows cost no compute.
+ */
+int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                   const void* B, int64_t ldb, const float* sb,
+                                   void* D, int64_t ldd, const int32_t* m_indices,
+                                   int M_total, int N, int K, int G,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * M-grouped masked GEMM (MoE decode under graph capture; pages:
+ * es.news.hada.io/topic?id=19459 "Dense y Grouped GEMM", masked layout: with a
+ * mask tensor only the valid regions are computed; GeekNews topic 19444: the CPU
+ * does not know the per-expert token counts).
+ *   A  e4m3 [G, M_max, K]: group g at A + g * M_max * lda.
+ *   sa fp32 [G][K/128][ld_sa], ld_sa >= M_max.
+ *   B  e4m3 [G, N, K]; sb fp32 [G][ceil(N/128)][K/128].
+ *   D  bf16 [G, M_max, N]: group g at D + g * M_max * ldd.
+ *   masked_m int32 [G] on the device: rows [0, masked_m[g]) of group g are
+ *      computed; rows at or beyond it are not written. Values are clamped to
+ *      [0, M_max]. The host never reads masked_m, so the call is graph-capturable.
+ *   expected_m: host-side hint of the typical masked_m (tile choice only).
+ *   G <= 1024.
+ */
+int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                               const void* B, int64_t ldb, const float* sb,
+                               void* D, int64_t ldd, const int32_t* masked_m,
+                               int G, int M_max, int N, int K, int expected_m,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of split-K workspace the call with these sizes may use (0 = never splits).
+ * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked). */
+size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m);
+
+/* Configuration the library would use for a call (no launch, no device access
+ * when fp8_gemm_set_num_cus() has been given a value). Returns FP8GEMM_OK. */
+int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m,
+                          size_t workspace_bytes, fp8gemm_config_t* out);
+
+/* Force the tile configuration of later calls (tuning and tests): block_m,
+ * block_n and split_k are used, grid and num_units are ignored. NULL restores
+ * automatic selection. Not thread-safe; process-wide.
+ * Returns FP8GEMM_ERR_CONFIG for a tile shape that has no kernel. */
+int fp8_gemm_force_config(const fp8gemm_config_t* cfg);
+
+/* Cap on the compute units the persistent grid is sized for (DeepGEMM's
+ * set_num_sms analog, "Utilidades y variables de entorno"). n <= 0 restores the
+ * device's own count. get returns the value in effect (0 if none is known yet). */
+int fp8_gemm_set_num_cus(int n);
+int fp8_gemm_get_num_cus(void);
+
+/* Row alignment of each expert segment in the contiguous layout: 128. */
+int fp8_gemm_get_mk_alignment_for_contiguous_layout(void);
+
+/* Smallest valid ld_sa for `rows` rows: rows rounded up to a multiple of 4. */
+int64_t fp8_gemm_scale_ld(int64_t rows);
+
+/* Number of output tiles of an M x N output cut into block_m x block_n tiles. */
+int64_t fp8_gemm_num_tiles(int64_t M, int64_t N, int block_m, int block_n);
+
+/* Static description of a status code. */
+const char* fp8_gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H_ */

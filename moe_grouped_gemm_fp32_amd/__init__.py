@@ -1,0 +1,253 @@
+"""FP8 (e4m3) block-scaled NT GEMM for AMD MI355X: Python binding of libfp8gemm.so.
+
+A thin ctypes layer over the C ABI declared in include/fp8gemm.h. It only
+marshals torch tensors (device pointers, strides, the current HIP stream) into
+the library's entry points; every step of the computation runs in the library's
+HIP kernels. PyTorch supplies device memory and streams. Importing works without
+a GPU; calling a GEMM needs the built library and a gfx950 device, and raises
+otherwise (there is no fallback path).
+
+Entry points (names follow the DeepGEMM pages' interface, bquan.live post
+9429818 "¿Cómo usarlo?" and es.news.hada.io/topic?id=19459 "Dense y Grouped
+GEMM"):
+  fp8_gemm_nt                       D = A . B^T
+  fp8_grouped_gemm_nt_contiguous    experts concatenated along M, m_indices per row
+  fp8_grouped_gemm_nt_masked        [G, M_max, K] input, masked_m[g] live rows
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "fp8_gemm_nt", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
+    "workspace_size", "make_workspace", "query_config", "force_config", "set_num_cus",
+    "get_num_cus", "get_mk_alignment_for_contiguous_layout", "scale_ld", "num_tiles",
+    "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED",
+    "Fp8GemmError",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8gemm.so")
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED = 0, 1, 2
+
+
+class Fp8GemmError(RuntimeError):
+    pass
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("grid", ctypes.c_int), ("num_units", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+_P, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "fp8_gemm_nt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_contiguous": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_masked": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
+    "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
+    "fp8_gemm_force_config": (_INT, [ctypes.POINTER(Config)]),
+    "fp8_gemm_set_num_cus": (_INT, [_INT]),
+    "fp8_gemm_get_num_cus": (_INT, []),
+    "fp8_gemm_get_mk_alignment_for_contiguous_layout": (_INT, []),
+    "fp8_gemm_scale_ld": (_I64, [_I64]),
+    "fp8_gemm_num_tiles": (_I64, [_I64, _I64, _INT, _INT]),
+    "fp8_gemm_status_string": (ctypes.c_char_p, [_INT]),
+}
+
+
+def lib():
+    """The loaded libfp8gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with moe_grouped_gemm_fp32_amd/build.py "
+                              "(or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8_gemm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Fp8GemmError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _bytes_view(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"FP8 operand must be uint8 (e4m3 bytes) or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def _common(A, sa, B, sb, D, rows_dim):
+    A, B = _bytes_view(A), _bytes_view(B)
+    dev = D.device
+    _require(dev.type == "cuda", "tensors must live on a GPU")
+    for name, t in (("A", A), ("sa", sa), ("B", B), ("sb", sb), ("D", D)):
+        _require(t.device == dev, f"{name} is on {t.device}, D on {dev}")
+        _require(t.stride(-1) == 1, f"{name} must have a unit inner stride")
+    _require(sa.dtype == torch.float32 and sb.dtype == torch.float32, "scales must be float32")
+    _require(D.dtype == torch.bfloat16, "D must be bfloat16")
+    _require(sb.is_contiguous(), "sb must be contiguous")
+    return A, B, dev
+
+
+def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """D[M, N] = A[M, K] . B[N, K]^T with 1x128 (sa [K/128, ld_sa]) and 128x128 (sb) scales.
+
+    A, B: e4m3 bytes (uint8 or float8_e4m3fn), row-major with unit inner stride.
+    sa: float32 [K/128, ld_sa], row stride ld_sa >= M. sb: float32 [ceil(N/128), K/128].
+    D: bfloat16 [M, N] (written in place and returned). workspace: optional
+    zero-initialised uint8 device buffer enabling split-K (see make_workspace).
+    """
+    A, B, dev = _common(A, sa, B, sb, D, 0)
+    M, K = A.shape
+    N = B.shape[0]
+    _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_gemm_nt(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                           _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
+    _check(st, "fp8_gemm_nt")
+    return D
+
+
+def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None):
+    """M-grouped contiguous GEMM: row r of D = A[r] . B[m_indices[r]]^T; rows with -1 untouched.
+
+    A [M_total, K]; sa float32 [K/128, >=M_total]; B [G, N, K]; sb [G, ceil(N/128), K/128];
+    D bfloat16 [M_total, N]; m_indices int32 [M_total] on the device.
+    """
+    A, B, dev = _common(A, sa, B, sb, D, 0)
+    Mt, K = A.shape
+    G, N, K2 = B.shape
+    _require(K2 == K and tuple(D.shape) == (Mt, N), "shape mismatch")
+    _require(B.is_contiguous(), "B must be contiguous [G, N, K]")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= Mt, "sa must be [K/128, >=M_total]")
+    _require(tuple(sb.shape) == (G, (N + 127) // 128, K // 128), "sb must be [G, ceil(N/128), K/128]")
+    _require(m_indices.dtype == torch.int32 and m_indices.numel() == Mt and m_indices.device == dev
+             and m_indices.is_contiguous(), "m_indices must be a contiguous int32 [M_total] device tensor")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_grouped_gemm_nt_contiguous(
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
+        _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
+    _check(st, "fp8_grouped_gemm_nt_contiguous")
+    return D
+
+
+def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, workspace=None, stream=None):
+    """M-grouped masked GEMM: D[g, m] = A[g, m] . B[g]^T for m < masked_m[g]; other rows untouched.
+
+    A [G, M_max, K]; sa float32 [G, K/128, ld_sa >= M_max]; B [G, N, K];
+    sb [G, ceil(N/128), K/128]; D bfloat16 [G, M_max, N]; masked_m int32 [G] on
+    the device (never read by the host); expected_m is a tiling hint.
+    """
+    A, B, dev = _common(A, sa, B, sb, D, 1)
+    G, M_max, K = A.shape
+    G2, N, K2 = B.shape
+    _require(G2 == G and K2 == K and tuple(D.shape) == (G, M_max, N), "shape mismatch")
+    for name, t in (("A", A), ("B", B), ("D", D), ("sa", sa)):
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(sa.dim() == 3 and sa.shape[0] == G and sa.shape[1] == K // 128 and sa.shape[2] >= M_max,
+             "sa must be [G, K/128, >=M_max]")
+    _require(tuple(sb.shape) == (G, (N + 127) // 128, K // 128), "sb must be [G, ceil(N/128), K/128]")
+    _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev,
+             "masked_m must be an int32 [G] device tensor")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_grouped_gemm_nt_masked(
+        _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
+        _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
+    _check(st, "fp8_grouped_gemm_nt_masked")
+    return D
+
+
+def workspace_size(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0) -> int:
+    return int(lib().fp8_gemm_workspace_size(kind, M, N, K, G, expected_m))
+
+
+def make_workspace(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0, device="cuda"):
+    """Zero-filled split-K workspace for calls of these sizes (None if never needed)."""
+    n = workspace_size(kind, M, N, K, G, expected_m)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def query_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0,
+                 workspace_bytes: int = 1 << 62) -> dict:
+    cfg = Config()
+    _check(lib().fp8_gemm_query_config(kind, M, N, K, G, expected_m, workspace_bytes, ctypes.byref(cfg)),
+           "fp8_gemm_query_config")
+    return cfg.as_dict()
+
+
+@contextlib.contextmanager
+def force_config(block_m: int, block_n: int, split_k: int = 1):
+    """Context manager forcing a tile configuration (tests and tuning)."""
+    cfg = Config(block_m, block_n, split_k, 0, 0)
+    _check(lib().fp8_gemm_force_config(ctypes.byref(cfg)), "fp8_gemm_force_config")
+    try:
+        yield
+    finally:
+        lib().fp8_gemm_force_config(None)
+
+
+def set_num_cus(n: int) -> None:
+    lib().fp8_gemm_set_num_cus(int(n))
+
+
+def get_num_cus() -> int:
+    return int(lib().fp8_gemm_get_num_cus())
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return int(lib().fp8_gemm_get_mk_alignment_for_contiguous_layout())
+
+
+def scale_ld(rows: int) -> int:
+    return int(lib().fp8_gemm_scale_ld(rows))
+
+
+def num_tiles(M: int, N: int, block_m: int, block_n: int) -> int:
+    return int(lib().fp8_gemm_num_tiles(M, N, block_m, block_n))

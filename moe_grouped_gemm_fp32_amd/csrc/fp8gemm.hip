@@ -1,0 +1,374 @@
+// Host side of libfp8gemm: argument checks, tile/split selection, persistent-grid
+// sizing and launch of the gfx950 kernels behind the C ABI in include/fp8gemm.h.
+//
+// Tile selection follows the pages' point that block shape, stage count and grid
+// should be chosen per shape so every compute unit has work (bquan.live post
+// 9429818, "¿Cómo usarlo?": dynamic block size / pipeline stage choice;
+// deepep.org/zh/deepgemm, 非对齐块大小: pick tiles that keep more SMs busy). On
+// MI355X that means filling 256 CUs: small-M shapes split K across workgroups and
+// reduce the FP32 partials in a fixed order; large shapes use 128x128 tiles.
+#include "fp8gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "fp8gemm_kernel.hpp"
+
+namespace {
+
+using fp8gemm::Params;
+
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256;
+
+struct DeviceInfo {
+  int cus = 0;
+  int status = 1;  // 1 = not queried, FP8GEMM_OK or FP8GEMM_ERR_DEVICE
+};
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_dev_mutex;
+std::atomic<int> g_num_cus_override{0};
+bool g_forced = false;
+fp8gemm_config_t g_forced_cfg{};
+
+int query_device(int* cus_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8GEMM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& d = g_devices[dev];
+  if (d.status == 1) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      d.status = FP8GEMM_ERR_DEVICE;
+    } else {
+      d.cus = prop.multiProcessorCount;
+      d.status = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? FP8GEMM_OK : FP8GEMM_ERR_DEVICE;
+    }
+  }
+  *cus_out = d.cus;
+  return d.status;
+}
+
+// CU count used for sizing: the override if set, else the device's (or the
+// MI355X default when no device is current, e.g. for host-only queries).
+int effective_cus(bool need_device, int* status) {
+  *status = FP8GEMM_OK;
+  int cus = 0;
+  if (need_device) {
+    *status = query_device(&cus);
+    if (*status != FP8GEMM_OK) return 0;
+  }
+  const int ov = g_num_cus_override.load();
+  if (ov > 0) return need_device ? std::min(ov, cus) : ov;
+  return cus > 0 ? cus : kDefaultCus;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct TileShape {
+  int bm, bn;
+};
+// Tile shapes with a compiled kernel.
+constexpr TileShape kTiles[] = {{64, 64}, {128, 64}, {64, 128}, {128, 128}};
+
+bool has_kernel(int bm, int bn) {
+  for (const auto& t : kTiles)
+    if (t.bm == bm && t.bn == bn) return true;
+  return false;
+}
+
+struct Plan {
+  int bm = 128, bn = 128, split = 1, kbps = 1, tiles_m = 0, tiles_n = 0;
+  int64_t units = 0;
+  int grid = 0;
+  size_t ws_bytes = 0;
+};
+
+// Workgroups per CU each tile shape is compiled for (register budget).
+constexpr int occupancy_of(int bm, int bn) { return bm * bn >= 128 * 128 ? 1 : 2; }
+
+size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
+  if (split <= 1) return 0;
+  return (size_t)tiles * split * bm * bn * sizeof(float) + (size_t)tiles * sizeof(int32_t);
+}
+
+// Choose tile shape and split for a call. `rows` is M (dense), M_total
+// (contiguous) or expected live rows per group (masked); `groups` multiplies the
+// m-tile count for masked.
+Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
+  Plan pl;
+  const int num_kb = K / fp8gemm::kBlockK;
+  if (g_forced) {
+    pl.bm = g_forced_cfg.block_m;
+    pl.bn = g_forced_cfg.block_n;
+    pl.split = std::max(1, g_forced_cfg.split_k);
+  } else {
+    int bm, bn;
+    if (kind == FP8GEMM_KIND_MASKED) {
+      const int live = std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows));
+      bm = 64;
+      const int64_t t128 = (int64_t)G * ceil_div(live, bm) * ceil_div(N, 128);
+      bn = t128 >= cus ? 128 : 64;
+    } else if (rows <= 64) {
+      bm = 64; bn = 64;
+    } else if (rows <= 128) {
+      bm = 128; bn = 64;
+    } else {
+      bm = 128; bn = 128;
+      if (ceil_div(rows, bm) * ceil_div(N, bn) < cus) bn = 64;
+    }
+    pl.bm = bm;
+    pl.bn = bn;
+    pl.split = 1;
+    if (kind != FP8GEMM_KIND_MASKED) {
+      const int64_t tiles = ceil_div(rows, bm) * ceil_div(N, bn);
+      if (tiles < cus && num_kb >= 4) {
+        int want = (int)std::min<int64_t>(ceil_div(cus, tiles), num_kb / 2);
+        want = std::max(1, want);
+        pl.split = want;
+      }
+    }
+  }
+  pl.kbps = (int)ceil_div(num_kb, pl.split);
+  pl.split = (int)ceil_div(num_kb, pl.kbps);  // no empty splits
+  pl.tiles_n = (int)ceil_div(N, pl.bn);
+  pl.tiles_m = (int)ceil_div(rows, pl.bm);
+  const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (kind == FP8GEMM_KIND_MASKED ? G : 1);
+  pl.ws_bytes = split_ws_bytes(tiles, pl.split, pl.bm, pl.bn);
+  if (pl.split > 1 && pl.ws_bytes > ws_avail && !g_forced) {
+    pl.split = 1;
+    pl.kbps = num_kb;
+    pl.ws_bytes = 0;
+  }
+  pl.units = tiles * pl.split;
+  const int64_t cap = (int64_t)cus * occupancy_of(pl.bm, pl.bn);
+  int64_t grid = std::min<int64_t>(pl.units, cap);
+  if (grid > fp8gemm::kNumXcd) grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;  // keep XCD mapping
+  pl.grid = (int)std::max<int64_t>(grid, 1);
+  return pl;
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const Params& p, int grid, hipStream_t stream) {
+  constexpr int WN = BN >= 128 ? 2 : (BM >= 128 ? 1 : 2);
+  constexpr int WM = 4 / WN;
+  constexpr int OCC = occupancy_of(BM, BN);
+  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<BM, BN, WM, WN, OCC>), dim3(grid), dim3(fp8gemm::kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream) {
+  if (pl.bm == 64 && pl.bn == 64) return launch_tile<64, 64>(p, pl.grid, stream);
+  if (pl.bm == 128 && pl.bn == 64) return launch_tile<128, 64>(p, pl.grid, stream);
+  if (pl.bm == 64 && pl.bn == 128) return launch_tile<64, 128>(p, pl.grid, stream);
+  if (pl.bm == 128 && pl.bn == 128) return launch_tile<128, 128>(p, pl.grid, stream);
+  return hipErrorInvalidValue;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_common(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                 const float* sb, void* D, int64_t ldd, int rows, int N, int K) {
+  if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
+  if (rows < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
+  if (lda < K || lda % 16 || ldb < K || ldb % 16) return FP8GEMM_ERR_LAYOUT;
+  if (ldd < N) return FP8GEMM_ERR_LAYOUT;
+  if (ld_sa < rows || ld_sa % 4) return FP8GEMM_ERR_LAYOUT;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 2) || !aligned(sa, 4) || !aligned(sb, 4))
+    return FP8GEMM_ERR_LAYOUT;
+  return FP8GEMM_OK;
+}
+
+void maybe_print(const char* what, int rows, int N, int K, int G, const Plan& pl) {
+  static const bool on = [] {
+    const char* e = std::getenv("FP8GEMM_PRINT_CONFIGS");
+    return e && *e && *e != '0';
+  }();
+  if (!on) return;
+  std::fprintf(stderr, "[fp8gemm] %s M=%d N=%d K=%d G=%d -> tile %dx%d split %d grid %d units %lld\n", what,
+               rows, N, K, G, pl.bm, pl.bn, pl.split, pl.grid, (long long)pl.units);
+}
+
+int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, int expected_m, void* workspace,
+        size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  const int cus = effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  const size_t ws_avail = workspace ? workspace_bytes : 0;
+  Plan pl = choose(kind, rows, N, K, G, expected_m, cus, ws_avail);
+  if (!has_kernel(pl.bm, pl.bn)) return FP8GEMM_ERR_CONFIG;
+  if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
+  maybe_print(name, rows, N, K, G, pl);
+  p.N = N;
+  p.K = K;
+  p.G = G;
+  p.kind = kind;
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  p.split_k = pl.split;
+  p.kb_per_split = pl.kbps;
+  p.num_kb = K / fp8gemm::kBlockK;
+  p.num_units = (int)pl.units;
+  p.group_m = 8;
+  p.vec_store = (p.ldd % 4 == 0) && aligned(p.D, 8);
+  if (pl.split > 1) {
+    const int64_t tiles = pl.units / pl.split;
+    p.ws = static_cast<float*>(workspace);
+    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                            (size_t)tiles * pl.split * pl.bm * pl.bn * sizeof(float));
+  }
+  if (pl.units == 0) return FP8GEMM_OK;
+  return launch(pl, p, stream) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+
+Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                   const float* sb, void* D, int64_t ldd) {
+  Params p{};
+  p.A = static_cast<const uint8_t*>(A);
+  p.sa = sa;
+  p.B = static_cast<const uint8_t*>(B);
+  p.sb = sb;
+  p.D = static_cast<uint16_t*>(D);
+  p.lda = lda;
+  p.ld_sa = ld_sa;
+  p.ldb = ldb;
+  p.ldd = ldd;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M;
+  return run(FP8GEMM_KIND_DENSE, "dense", p, M, N, K, 1, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                   int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* m_indices,
+                                   int M_total, int N, int K, int G, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_total, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (!m_indices) return FP8GEMM_ERR_NULL;
+  if (G <= 0) return FP8GEMM_ERR_SHAPE;
+  if (M_total == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M_total;
+  p.m_indices = m_indices;
+  p.b_gstride = (int64_t)N * ldb;
+  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  // tiles must not straddle two 128-row expert blocks
+  if (g_forced && 128 % g_forced_cfg.block_m != 0) return FP8GEMM_ERR_CONFIG;
+  return run(FP8GEMM_KIND_CONTIGUOUS, "contiguous", p, M_total, N, K, G, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                               int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G,
+                               int M_max, int N, int K, int expected_m, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (!masked_m) return FP8GEMM_ERR_NULL;
+  if (G <= 0 || G > fp8gemm::kMaxGroups || M_max <= 0) return FP8GEMM_ERR_SHAPE;
+  if (g_forced && g_forced_cfg.split_k > 1) return FP8GEMM_ERR_CONFIG;  // masked never splits K
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M_max;
+  p.masked_m = masked_m;
+  p.a_gstride = (int64_t)M_max * lda;
+  p.sa_gstride = (int64_t)(K / 128) * ld_sa;
+  p.b_gstride = (int64_t)N * ldb;
+  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  p.d_gstride = (int64_t)M_max * ldd;
+  (void)workspace;
+  (void)workspace_bytes;
+  return run(FP8GEMM_KIND_MASKED, "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream);
+}
+
+size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 || kind == FP8GEMM_KIND_MASKED) return 0;
+  int st;
+  const int cus = effective_cus(false, &st);
+  const Plan pl = choose(kind, M, N, K, std::max(G, 1), expected_m, cus, SIZE_MAX);
+  return pl.split > 1 ? pl.ws_bytes : 0;
+}
+
+int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m, size_t workspace_bytes,
+                          fp8gemm_config_t* out) {
+  if (!out) return FP8GEMM_ERR_NULL;
+  if (M < 0 || N <= 0 || K <= 0 || K % 128 || G <= 0) return FP8GEMM_ERR_SHAPE;
+  int st;
+  const int cus = effective_cus(false, &st);
+  const Plan pl = choose(kind, M, N, K, G, expected_m, cus,
+                         kind == FP8GEMM_KIND_MASKED ? 0 : workspace_bytes);
+  out->block_m = pl.bm;
+  out->block_n = pl.bn;
+  out->split_k = pl.split;
+  out->grid = pl.grid;
+  out->num_units = (int)pl.units;
+  return FP8GEMM_OK;
+}
+
+int fp8_gemm_force_config(const fp8gemm_config_t* cfg) {
+  if (!cfg) {
+    g_forced = false;
+    return FP8GEMM_OK;
+  }
+  if (!has_kernel(cfg->block_m, cfg->block_n) || cfg->split_k < 1) return FP8GEMM_ERR_CONFIG;
+  g_forced_cfg = *cfg;
+  g_forced = true;
+  return FP8GEMM_OK;
+}
+
+int fp8_gemm_set_num_cus(int n) {
+  g_num_cus_override.store(n > 0 ? n : 0);
+  return FP8GEMM_OK;
+}
+
+int fp8_gemm_get_num_cus(void) {
+  const int ov = g_num_cus_override.load();
+  if (ov > 0) return ov;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  return g_devices[dev].status == FP8GEMM_OK ? g_devices[dev].cus : 0;
+}
+
+int fp8_gemm_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int64_t fp8_gemm_scale_ld(int64_t rows) { return rows <= 0 ? 0 : (rows + 3) / 4 * 4; }
+
+int64_t fp8_gemm_num_tiles(int64_t M, int64_t N, int block_m, int block_n) {
+  if (M <= 0 || N <= 0 || block_m <= 0 || block_n <= 0) return 0;
+  return ceil_div(M, block_m) * ceil_div(N, block_n);
+}
+
+const char* fp8_gemm_status_string(int status) {
+  switch (status) {
+    case FP8GEMM_OK: return "ok";
+    case FP8GEMM_ERR_NULL: return "null pointer argument";
+    case FP8GEMM_ERR_SHAPE: return "invalid shape (sizes must be positive, K a multiple of 128)";
+    case FP8GEMM_ERR_LAYOUT: return "invalid stride, leading dimension or alignment";
+    case FP8GEMM_ERR_WORKSPACE: return "workspace too small for the forced split-K configuration";
+    case FP8GEMM_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
+    case FP8GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case FP8GEMM_ERR_CONFIG: return "invalid forced tile configuration";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -99,9 +99,12 @@ def random_bytes(shape, gen: torch.Generator, device) -> torch.Tensor:
 
 
 def _small_int_codes(shape, values: Sequence[int], probs: Sequence[float], gen, device):
-    p = torch.tensor(probs, dtype=torch.float32, device=device)
-    idx = torch.multinomial(p, int(math.prod(shape)), replacement=True, generator=gen)
-    v = torch.tensor(values, dtype=torch.float32, device=device)[idx].reshape(shape)
+    """e4m3 codes of integers drawn from ``values`` with probabilities ``probs``."""
+    edges = torch.tensor(list(probs), dtype=torch.float64).cumsum(0)[:-1]
+    edges = (edges / sum(probs)).to(torch.float32).to(device)
+    u = torch.rand(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    idx = torch.bucketize(u, edges, right=True)
+    v = torch.tensor(list(values), dtype=torch.float32, device=device)[idx]
     return _to_e4m3_bytes(v)
 
 

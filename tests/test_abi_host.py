@@ -1,0 +1,132 @@
+"""Host-side checks of libfp8gemm.so that need no GPU: every symbol the header
+declares is exported, argument validation returns the documented codes without
+launching, and the tile/split planner keeps its invariants."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_fp32_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8gemm.h")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+CONFIG2 = [(m, n, k) for m in (64, 128, 4096)
+           for (n, k) in ((2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048))]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:const\s+char\s*\*|int64_t|size_t|int)\s+(fp8_\w+)\s*\(", text, re.M)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(fg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fg._SIGS), "binding and header disagree"
+
+
+def test_status_strings_and_utilities():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert fg.status_string(code) and fg.status_string(code) != "unknown status"
+    assert fg.status_string(-99) == "unknown status"
+    assert fg.get_mk_alignment_for_contiguous_layout() == 128
+    assert [fg.scale_ld(r) for r in (1, 4, 5, 2111, 2112)] == [4, 4, 8, 2112, 2112]
+
+
+def test_tile_count_worked_example_from_pages():
+    # deepep.org/zh/deepgemm, 核心优化技术 / 非对齐块大小: on 132 SMs, BLOCK_N=112 keeps
+    # 128 busy where BLOCK_N=128 keeps 112 (M=256, N=7168, BLOCK_M=128)
+    rows = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "unaligned_block_tiles.txt"))]
+    rows = [r for r in rows if r]
+    assert len(rows) == 2
+    for M, N, bm, bn, busy in ([int(x) for x in r] for r in rows):
+        assert min(fg.num_tiles(M, N, bm, bn), 132) == busy
+
+
+P = ctypes.c_void_p
+
+
+def _dense(A=1 << 20, lda=7168, sa=1 << 20, ld_sa=64, B=1 << 20, ldb=7168, sb=1 << 20, D=1 << 20, ldd=2112,
+           M=64, N=2112, K=7168):
+    mk = lambda v: P(v) if v else None
+    return fg.lib().fp8_gemm_nt(mk(A), lda, mk(sa), ld_sa, mk(B), ldb, mk(sb), mk(D), ldd, M, N, K, None, 0, None)
+
+
+def test_argument_validation_codes_without_launch():
+    assert _dense(A=0) == -1 and _dense(sa=0) == -1 and _dense(D=0) == -1
+    assert _dense(K=100) == -2 and _dense(N=0) == -2 and _dense(M=-1) == -2
+    assert _dense(lda=7000) == -3 and _dense(ldb=7169) == -3 and _dense(ldd=2100) == -3
+    assert _dense(ld_sa=63) == -3 and _dense(ld_sa=66) == -3
+    assert _dense(A=(1 << 20) + 8) == -3 and _dense(D=(1 << 20) + 1) == -3
+    assert _dense(M=0) == 0  # empty problem: nothing to do
+    L = fg.lib()
+    # contiguous: missing m_indices / bad G; masked: missing masked_m / G out of range
+    args = (P(1 << 20), 7168, P(1 << 20), 64, P(1 << 20), 7168, P(1 << 20), P(1 << 20), 4096)
+    assert L.fp8_grouped_gemm_nt_contiguous(*args, None, 64, 4096, 7168, 4, None, 0, None) == -1
+    assert L.fp8_grouped_gemm_nt_contiguous(*args, P(1 << 20), 64, 4096, 7168, 0, None, 0, None) == -2
+    assert L.fp8_grouped_gemm_nt_masked(*args, None, 4, 64, 4096, 7168, 32, None, 0, None) == -1
+    assert L.fp8_grouped_gemm_nt_masked(*args, P(1 << 20), 1025, 64, 4096, 7168, 32, None, 0, None) == -2
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _dense() == -5
+
+
+@pytest.fixture
+def cus256():
+    fg.set_num_cus(256)
+    yield
+    fg.set_num_cus(0)
+
+
+@pytest.mark.parametrize("M,N,K", CONFIG2)
+def test_planner_invariants_on_dense_shapes(cus256, M, N, K):
+    cfg = fg.query_config(fg.KIND_DENSE, M, N, K)
+    bm, bn, s = cfg["block_m"], cfg["block_n"], cfg["split_k"]
+    tiles = fg.num_tiles(M, N, bm, bn)
+    assert cfg["num_units"] == tiles * s
+    nkb = K // 128
+    assert 1 <= s <= nkb and (s == 1 or nkb % s == 0 or -(-nkb // s) * (s - 1) < nkb)
+    # every split owns at least one K block
+    kbps = -(-nkb // s)
+    assert kbps * (s - 1) < nkb
+    # small problems are spread over (at least nearly) all CUs
+    if tiles < 256:
+        assert cfg["num_units"] >= 224 or s == nkb // 2
+    assert cfg["grid"] <= cfg["num_units"] and cfg["grid"] <= 512
+    ws = fg.workspace_size(fg.KIND_DENSE, M, N, K)
+    assert (ws > 0) == (s > 1)
+    if s > 1:
+        assert ws >= tiles * s * bm * bn * 4 + tiles * 4
+        # without a workspace the call falls back to no split
+        assert fg.query_config(fg.KIND_DENSE, M, N, K, workspace_bytes=0)["split_k"] == 1
+
+
+def test_planner_masked_and_contiguous(cus256):
+    for G in (1, 2, 4, 8, 16):
+        for N, K in ((4096, 7168), (7168, 2048)):
+            cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
+            assert cfg["split_k"] == 1 and 128 % cfg["block_m"] == 0
+            assert fg.workspace_size(fg.KIND_MASKED, 4096, N, K, G, 256) == 0
+    cfg = fg.query_config(fg.KIND_CONTIGUOUS, 32768, 4096, 7168, 4)
+    assert 128 % cfg["block_m"] == 0
+
+
+def test_force_config_validation():
+    L = fg.lib()
+    bad = fg.Config(96, 64, 1, 0, 0)
+    assert L.fp8_gemm_force_config(ctypes.byref(bad)) == -7
+    bad = fg.Config(64, 64, 0, 0, 0)
+    assert L.fp8_gemm_force_config(ctypes.byref(bad)) == -7
+    with fg.force_config(64, 128, 2):
+        assert fg.query_config(fg.KIND_DENSE, 100, 300, 1024)["block_n"] == 128
+    assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168)["block_m"] == 128

@@ -1,0 +1,124 @@
+"""GPU parity of the dense FP8 NT GEMM (fp8_gemm_nt through the C ABI) against the
+CPU oracle: every compiled tile shape and split-K factor on small shapes, ragged
+edges, bit-exact integer cases, and the full-size DeepSeek-V3-like shape list on
+sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_fp32_amd as fg
+import oracle
+import synth
+from parity_util import SENT, assert_bit_exact, bits_of, compare, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TILES = [(64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (64, 64, 2), (128, 64, 3), (128, 128, 4)]
+CONFIG2_NK = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]
+
+
+def run_dense(c, forced=None, ws=True):
+    D = c["D"].clone()
+    M, N, K = c["M"], c["N"], c["K"]
+    work = None
+    if ws:
+        nbytes = fg.workspace_size(fg.KIND_DENSE, M, N, K)
+        if forced is not None and forced[2] > 1:
+            tiles = fg.num_tiles(M, N, forced[0], forced[1])
+            nbytes = tiles * forced[2] * forced[0] * forced[1] * 4 + tiles * 4
+        work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
+    if forced is None:
+        fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+    else:
+        with fg.force_config(*forced):
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+    torch.cuda.synchronize()
+    return D, work
+
+
+@pytest.mark.parametrize("kind", ["normal", "e1", "e2", "e3"])
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: "%dx%d_s%d" % t)
+def test_config1_every_tile(cuda_device, kind, tile):
+    c = synth.dense_case(128, 256, 512, seed=1000 + 1, device=cuda_device, kind=kind)
+    D, _ = run_dense(c, forced=tile)
+    ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
+    compare(kind, bits_of(D), ref, f"config1 {kind} {tile}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (63, 130, 256), (65, 200, 384), (200, 2112, 512),
+                                   (129, 96, 1024), (257, 320, 640), (17, 16, 128), (300, 1000, 1280)])
+@pytest.mark.parametrize("kind", ["normal", "e1"])
+def test_ragged_shapes_auto_and_forced(cuda_device, M, N, K, kind):
+    c = synth.dense_case(M, N, K, seed=7 * M + N + K, device=cuda_device, kind=kind)
+    ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
+    D, _ = run_dense(c)
+    compare(kind, bits_of(D), ref, f"auto {M}x{N}x{K}")
+    for tile in [(64, 64, 1), (128, 128, 2), (64, 128, 3)]:
+        D, _ = run_dense(c, forced=tile)
+        compare(kind, bits_of(D), ref, f"{tile} {M}x{N}x{K}")
+
+
+def test_split_k_is_deterministic_and_workspace_self_resets(cuda_device):
+    c = synth.dense_case(64, 2112, 7168, seed=31, device=cuda_device)
+    ws_n = fg.workspace_size(fg.KIND_DENSE, 64, 2112, 7168)
+    assert ws_n > 0
+    work = torch.zeros(ws_n, dtype=torch.uint8, device=cuda_device)
+    outs = []
+    for _ in range(3):
+        D = c["D"].clone()
+        fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+        torch.cuda.synchronize()
+        outs.append(bits_of(D))
+        cfg = fg.query_config(fg.KIND_DENSE, 64, 2112, 7168)
+        tiles = cfg["num_units"] // cfg["split_k"]
+        counters = work[tiles * cfg["split_k"] * cfg["block_m"] * cfg["block_n"] * 4:][: tiles * 4]
+        assert int(counters.count_nonzero()) == 0, "split-K counters must be left at zero"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    # without a workspace the call runs unsplit and agrees within tolerance
+    D = c["D"].clone()
+    fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, None)
+    torch.cuda.synchronize()
+    rows = sample_rows(64, 16, 3)
+    ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(2112))
+    compare("normal", bits_of(D)[rows], ref, "unsplit")
+    compare("normal", outs[0][rows], ref, "split")
+
+
+@pytest.mark.parametrize("M", [64, 128, 4096])
+@pytest.mark.parametrize("N,K", CONFIG2_NK)
+def test_config2_full_size_sampled(cuda_device, M, N, K):
+    c = synth.dense_case(M, N, K, seed=2000 + M + N + K, device=cuda_device, a_std=1.0, b_std=0.02)
+    D, _ = run_dense(c)
+    bits = bits_of(D)
+    assert not np.any(bits == SENT), "every output must be written"
+    rows = sample_rows(M, 12, M + N)
+    ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))
+    compare("normal", bits[rows], ref, f"config2 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (128, 7168, 2048), (4096, 4096, 7168), (4096, 32768, 512)])
+def test_config2_exact_case_full_size_sampled(cuda_device, M, N, K):
+    c = synth.dense_case(M, N, K, seed=3000 + M + N, device=cuda_device, kind="e1")
+    D, _ = run_dense(c)
+    rows = sample_rows(M, 8, K)
+    cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
+    ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, cols)
+    assert_bit_exact(bits_of(D)[np.ix_(rows, cols)], ref, f"e1 M={M} N={N} K={K}")
+
+
+def test_strided_operands(cuda_device):
+    # leading dimensions larger than the logical sizes
+    M, N, K = 96, 192, 384
+    c = synth.dense_case(M, N, K, seed=77, device=cuda_device)
+    A = torch.zeros(M, K + 128, dtype=torch.uint8, device=cuda_device)
+    A[:, :K] = c["A"]
+    B = torch.zeros(N, K + 256, dtype=torch.uint8, device=cuda_device)
+    B[:, :K] = c["B"]
+    sa = torch.zeros(K // 128, 128, dtype=torch.float32, device=cuda_device)
+    sa[:, :c["sa"].shape[1]] = c["sa"]
+    Dbig = synth.sentinel_output((M, N + 64), cuda_device)
+    fg.fp8_gemm_nt(A[:, :K], sa, B[:, :K], c["sb"], Dbig[:, :N])
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
+    compare("normal", bits_of(Dbig)[:, :N], ref, "strided")
+    assert np.all(bits_of(Dbig)[:, N:] == SENT), "columns beyond N must not be written"
