@@ -28,6 +28,8 @@ def hipcc() -> str:
 def command(out: str, extra=()) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the FP32 promotion FMAs read them directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), *extra, SRC, "-o", out]
 
 

@@ -71,17 +71,6 @@ int effective_cus(bool need_device, int* status) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-struct TileShape {
-  int bm, bn;
-};
-// Tile shapes with a compiled kernel.
-constexpr TileShape kTiles[] = {{64, 64}, {128, 64}, {64, 128}, {128, 128}};
-
-bool has_kernel(int bm, int bn) {
-  for (const auto& t : kTiles)
-    if (t.bm == bm && t.bn == bn) return true;
-  return false;
-}
 
 struct Plan {
   int bm = 128, bn = 128, split = 1, kbps = 1, tiles_m = 0, tiles_n = 0;
@@ -90,8 +79,20 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-// Workgroups per CU each tile shape is compiled for (register budget).
-constexpr int occupancy_of(int bm, int bn) { return bm * bn >= 128 * 128 ? 1 : 2; }
+// Compiled variants: tile shape, wave layout and LDS ring depth. Every variant
+// uses about 140 KB of LDS, so one workgroup runs per CU.
+struct Variant {
+  int bm, bn, waves_m, waves_n, stages;
+};
+constexpr Variant kVariants[] = {
+    {64, 64, 2, 2, 8}, {128, 64, 2, 2, 6}, {64, 128, 2, 2, 6}, {128, 128, 2, 2, 4}};
+constexpr int kOccupancy = 1;
+
+bool has_kernel(int bm, int bn) {
+  for (const auto& v : kVariants)
+    if (v.bm == bm && v.bn == bn) return true;
+  return false;
+}
 
 size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
   if (split <= 1) return 0;
@@ -147,29 +148,29 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     pl.ws_bytes = 0;
   }
   pl.units = tiles * pl.split;
-  const int64_t cap = (int64_t)cus * occupancy_of(pl.bm, pl.bn);
+  const int64_t cap = (int64_t)cus * kOccupancy;
   int64_t grid = std::min<int64_t>(pl.units, cap);
   if (grid > fp8gemm::kNumXcd) grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;  // keep XCD mapping
   pl.grid = (int)std::max<int64_t>(grid, 1);
   return pl;
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(const Params& p, int grid, hipStream_t stream) {
-  constexpr int WN = BN >= 128 ? 2 : (BM >= 128 ? 1 : 2);
-  constexpr int WM = 4 / WN;
-  constexpr int OCC = occupancy_of(BM, BN);
-  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<BM, BN, WM, WN, OCC>), dim3(grid), dim3(fp8gemm::kThreads), 0,
-                     stream, p);
+template <int I>
+hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
+  constexpr Variant v = kVariants[I];
+  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, kOccupancy>),
+                     dim3(grid), dim3(fp8gemm::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int I = 0>
 hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream) {
-  if (pl.bm == 64 && pl.bn == 64) return launch_tile<64, 64>(p, pl.grid, stream);
-  if (pl.bm == 128 && pl.bn == 64) return launch_tile<128, 64>(p, pl.grid, stream);
-  if (pl.bm == 64 && pl.bn == 128) return launch_tile<64, 128>(p, pl.grid, stream);
-  if (pl.bm == 128 && pl.bn == 128) return launch_tile<128, 128>(p, pl.grid, stream);
-  return hipErrorInvalidValue;
+  if constexpr (I < (int)(sizeof(kVariants) / sizeof(kVariants[0]))) {
+    if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn) return launch_variant<I>(p, pl.grid, stream);
+    return launch<I + 1>(pl, p, stream);
+  } else {
+    return hipErrorInvalidValue;
+  }
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -183,6 +184,9 @@ int check_common(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   if (ld_sa < rows || ld_sa % 4) return FP8GEMM_ERR_LAYOUT;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 2) || !aligned(sa, 4) || !aligned(sb, 4))
     return FP8GEMM_ERR_LAYOUT;
+  // the kernels address rows of one operand (one group) with 32-bit byte offsets
+  if ((int64_t)std::max(rows - 1, 0) * lda + K > (int64_t)UINT32_MAX) return FP8GEMM_ERR_SHAPE;
+  if ((int64_t)(N - 1) * ldb + K > (int64_t)UINT32_MAX) return FP8GEMM_ERR_SHAPE;
   return FP8GEMM_OK;
 }
 

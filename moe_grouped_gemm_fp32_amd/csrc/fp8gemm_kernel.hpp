@@ -4,9 +4,12 @@
 // kernels, rasterised for L2 reuse).
 //
 // Per work unit (one BM x BN output tile, or one K-slice of it under split-K):
-//   for every 128-wide K block kb (one scale block, one MFMA deep):
-//     stage A[BM x 128] and B[BN x 128] bytes HBM -> registers -> LDS (2 stages,
-//       XOR-swizzled 16-byte chunks so fragment reads spread over the banks);
+//   a STAGES-deep ring of LDS stages, each holding one 128-wide K block: the A tile
+//   [BM x 128 B], the B tile [BN x 128 B] and that block's scales. Stages are filled
+//   by gfx950 direct-to-LDS loads (global_load_lds_dwordx4 / _dword), so up to
+//   STAGES-1 K blocks are in flight per workgroup without holding any registers;
+//   completion is tracked with explicit vmcnt waits and raw s_barrier.
+//   For every K block kb:
 //     t = v_mfma_f32_16x16x128_f8f6f4(B frag, A frag, 0)      -- exact FP8 products
 //     acc += t * (sa[kb][m] * sb[n/128][kb])                   -- FP32 promotion
 //   then round acc to BF16 (nearest-even) and store live rows.
@@ -24,6 +27,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace fp8gemm {
 
@@ -90,10 +95,58 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int gm, 
   tn = r / gs;
 }
 
-// Swizzled byte offset of 16-byte chunk `c` (0..7) of LDS row `row` (128 bytes/row).
+// Byte offset of 16-byte chunk `c` (0..7) of LDS row `row` (128 bytes per row):
+// chunk c is stored at position c ^ (row & 7) so the 16 rows a fragment read
+// touches spread over all bank groups.
 __device__ __forceinline__ int swz(int row, int c) { return row * kBlockK + ((c ^ (row & 7)) << 4); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int OCC>
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which would drain
+// every outstanding load); the empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 32-bit LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS loads: every lane reads `bytes` from its own global address and the
+// wave writes them to LDS at m0 + lane * bytes. Issued as asm so the compiler does
+// not treat them as LDS stores it must drain before every LDS read; completion is
+// tracked by the caller's explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Wait until at most min(n, MAXN) groups of LPS loads are outstanding.
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<LPS * MAXN>();
+    else wait_stages<LPS, MAXN - 1>(n);
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OCC>
 __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p) {
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
   constexpr int WTM = BM / WAVES_M;  // wave tile rows
@@ -102,14 +155,19 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
   constexpr int TN = WTN / 16;
   static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   static_assert(kBlockK % WTN == 0, "a wave's columns must share one 128-column scale block");
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && BM <= 128, "tile load split");
+  static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
   constexpr int B_BYTES = BN * kBlockK;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LD = A_BYTES / (16 * kThreads);  // 16-byte chunks per thread per kb
-  constexpr int B_LD = B_BYTES / (16 * kThreads);
-  static_assert(A_LD * 16 * kThreads == A_BYTES && B_LD * 16 * kThreads == B_BYTES, "tile load split");
+  constexpr int SC_FLOATS = 4 * 64;                 // per stage: 64 scale slots per wave
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_FLOATS * 4;
+  constexpr int A_INSTR = BM / 32;                  // 1 KB direct-to-LDS loads per wave per stage
+  constexpr int B_INSTR = BN / 32;
+  constexpr int LPS = A_INSTR + B_INSTR + 1;        // + one scale load
+  constexpr int SA_PER_WAVE = BM / 4;               // activation scales loaded by each wave
+  static_assert(LPS * (STAGES - 1) < 64, "vmcnt capacity");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE];
   __shared__ int s_pre[kMaxGroups + 1];  // masked: prefix sums of live m-tiles per group
   __shared__ int s_info;
 
@@ -136,7 +194,6 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
       local[q] = run;
       run += t;
     }
-    // inclusive scan of per-thread totals (Hillis-Steele over 256 entries)
     __shared__ int s_scan[kThreads];
     s_scan[tid] = run;
     __syncthreads();
@@ -198,58 +255,54 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
     }
 
     const int kb0 = split * p.kb_per_split;
-    const int kb1 = min(p.num_kb, kb0 + p.kb_per_split);
-    const uint8_t* Ag = p.A + (p.kind == kMasked ? (int64_t)g * p.a_gstride : 0);
-    const float* sag = p.sa + (p.kind == kMasked ? (int64_t)g * p.sa_gstride : 0);
-    const uint8_t* Bg = p.B + (int64_t)g * p.b_gstride;
-    const float* sbg = p.sb + (int64_t)g * p.sb_gstride;
+    const int nk = min(p.num_kb, kb0 + p.kb_per_split) - kb0;
+    const uint8_t* Ag = p.A + (p.kind == kMasked ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK;
+    const float* sag = p.sa + (p.kind == kMasked ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa;
+    const uint8_t* Bg = p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK;
+    const float* sbg = p.sb + (int64_t)g * p.sb_gstride + kb0;
 
-    // ---- global -> LDS copy plan: thread owns fixed 16-byte chunks of each tile
-    const uint8_t* a_src[A_LD];
-    int a_dst[A_LD];
+    // ---- direct-to-LDS load plan. Load instruction r of this wave fills 8 rows
+    // (1 KB) of a stage: lane l brings row 8*grp + l/8, logical chunk
+    // (l & 7) ^ (l >> 3), i.e. LDS chunk l & 7 of that row (the swizzle above).
+    const int lrow = lane >> 3;
+    const int lchunk = ((lane & 7) ^ lrow) << 4;
+    uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
-    for (int r = 0; r < A_LD; ++r) {
-      const int q = tid + r * kThreads;
-      const int row = q >> 3, c = q & 7;
+    for (int r = 0; r < A_INSTR; ++r) {
+      const int row = (r * 4 + wave) * 8 + lrow;
       const int grow = min(m0 + row, p.M - 1);  // rows past the end: clamped, results unused
-      a_src[r] = Ag + (int64_t)grow * p.lda + c * 16;
-      a_dst[r] = swz(row, c);
+      a_off[r] = (uint32_t)(grow * p.lda) + lchunk;
     }
-    const uint8_t* b_src[B_LD];
-    int b_dst[B_LD];
 #pragma unroll
-    for (int r = 0; r < B_LD; ++r) {
-      const int q = tid + r * kThreads;
-      const int row = q >> 3, c = q & 7;
+    for (int r = 0; r < B_INSTR; ++r) {
+      const int row = (r * 4 + wave) * 8 + lrow;
       const int grow = min(n0 + row, p.N - 1);
-      b_src[r] = Bg + (int64_t)grow * p.ldb + c * 16;
-      b_dst[r] = A_BYTES + swz(row, c);
+      b_off[r] = (uint32_t)(grow * p.ldb) + lchunk;
     }
+    // scale load: lanes [0, BM/4) bring activation scales of rows wave*BM/4 + lane,
+    // lane 63 brings this wave's weight scale, other lanes repeat lane 0's address
+    const float* sc_src;
+    {
+      const int wave_col = min(n0 + wn * WTN, p.N - 1);
+      if (lane == 63) {
+        sc_src = sbg + (int64_t)(wave_col / kBlockK) * p.num_kb;
+      } else {
+        const int row = wave * SA_PER_WAVE + (lane < SA_PER_WAVE ? lane : 0);
+        sc_src = sag + min(m0 + row, p.M - 1);
+      }
+    }
+    const int64_t sc_step = lane == 63 ? 1 : p.ld_sa;  // per K block
 
-    // rows / scale indices of this lane
-    int sa_row[TM];
+    const uint32_t ring = lds_addr(smem);
+    auto issue = [&](int i, int stage) {  // load K block kb0 + i into `stage`
+      const uint32_t base = ring + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa_row[i] = min(m0 + wm * WTM + 16 * i + (lane & 15), p.M - 1);
-    const int sb_row = min(n0 + wn * WTN, p.N - 1) / kBlockK;
-    const float* sb_ptr = sbg + (int64_t)sb_row * p.num_kb;
-
-    v4i ra[A_LD], rb[B_LD];
-    float sa_next[TM], sb_next;
-    auto gload = [&](int kb) {
+      for (int r = 0; r < A_INSTR; ++r)
+        dma16(Ag + (int64_t)i * kBlockK + a_off[r], base + (r * 4 + wave) * 1024);
 #pragma unroll
-      for (int r = 0; r < A_LD; ++r) ra[r] = *reinterpret_cast<const v4i*>(a_src[r] + (int64_t)kb * kBlockK);
-#pragma unroll
-      for (int r = 0; r < B_LD; ++r) rb[r] = *reinterpret_cast<const v4i*>(b_src[r] + (int64_t)kb * kBlockK);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa_next[i] = sag[(int64_t)kb * p.ld_sa + sa_row[i]];
-      sb_next = sb_ptr[kb];
-    };
-    auto lstore = [&](int stage) {
-      uint8_t* base = smem + stage * STAGE;
-#pragma unroll
-      for (int r = 0; r < A_LD; ++r) *reinterpret_cast<v4i*>(base + a_dst[r]) = ra[r];
-#pragma unroll
-      for (int r = 0; r < B_LD; ++r) *reinterpret_cast<v4i*>(base + b_dst[r]) = rb[r];
+      for (int r = 0; r < B_INSTR; ++r)
+        dma16(Bg + (int64_t)i * kBlockK + b_off[r], base + A_BYTES + (r * 4 + wave) * 1024);
+      dma4(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256);
     };
 
     v4f acc[TM][TN];
@@ -258,89 +311,143 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (kb0 < kb1) {
-      gload(kb0);
-      lstore(0);
-    }
-    __syncthreads();
-
-    const int frow = lane & 15;        // fragment row within a 16-row subtile
+    const int frow = lane & 15;          // fragment row within a 16-row subtile
     const int fchunk = (lane >> 4) * 2;  // first of the lane's two 16-byte K chunks
-    for (int kb = kb0; kb < kb1; ++kb) {
-      const int cur = (kb - kb0) & 1;
-      float s[TM];
+    int sa_slot[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) s[i] = sa_next[i] * sb_next;
-      if (kb + 1 < kb1) gload(kb + 1);
-
-      const uint8_t* sA = smem + cur * STAGE;
+    for (int t = 0; t < TM; ++t) {
+      const int row = wm * WTM + 16 * t + frow;
+      sa_slot[t] = (row / SA_PER_WAVE) * 64 + row % SA_PER_WAVE;
+    }
+    // fragments and scales of one stage, read from LDS into registers
+    v8i fa[2][TM], fb[2][TN];
+    float sc[2][TM];
+    auto read_stage = [&](int stage, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
+      const uint8_t* sA = smem + stage * STAGE;
       const uint8_t* sB = sA + A_BYTES;
-      v8i fa[TM], fb[TN];
+      const float* sS = reinterpret_cast<const float*>(sB + B_BYTES);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WTM + 16 * i + frow;
+      for (int t = 0; t < TM; ++t) {
+        const int row = wm * WTM + 16 * t + frow;
         const v4i lo = *reinterpret_cast<const v4i*>(sA + swz(row, fchunk));
         const v4i hi = *reinterpret_cast<const v4i*>(sA + swz(row, fchunk + 1));
-        fa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fa[buf][t] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int row = wn * WTN + 16 * j + frow;
         const v4i lo = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk));
         const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
-        fb[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fb[buf][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+      const float sbv = sS[wave * 64 + 63];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      for (int t = 0; t < TM; ++t) sc[buf][t] = sS[sa_slot[t]] * sbv;
+    };
+    // one K block from registers: MFMAs in batches of TN (one A subtile), each
+    // batch's promotion FMAs issued behind the next batch's MFMAs
+    auto compute = [&](auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
+      v4f r[2][TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              fb[j], fa[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          acc[i][j][0] = __builtin_fmaf(t[0], s[i], acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(t[1], s[i], acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(t[2], s[i], acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(t[3], s[i], acc[i][j][3]);
+      for (int t = 0; t <= TM; ++t) {
+        if (t < TM) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            r[t & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fb[buf][j], fa[buf][t], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        }
+        if (t > 0) {
+          const int q = t - 1;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            acc[q][j][0] = __builtin_fmaf(r[q & 1][j][0], sc[buf][q], acc[q][j][0]);
+            acc[q][j][1] = __builtin_fmaf(r[q & 1][j][1], sc[buf][q], acc[q][j][1]);
+            acc[q][j][2] = __builtin_fmaf(r[q & 1][j][2], sc[buf][q], acc[q][j][2]);
+            acc[q][j][3] = __builtin_fmaf(r[q & 1][j][3], sc[buf][q], acc[q][j][3]);
+          }
         }
       }
-      if (kb + 1 < kb1) lstore(cur ^ 1);
-      __syncthreads();
+    };
+
+    // Ring schedule: stage i lives in slot i % STAGES. Before computing stage i
+    // (from registers) the wave reads stage i+1 into its other register buffer, and
+    // the slot of stage i (already in registers everywhere) is refilled with
+    // stage i + STAGES.
+    // all waves are done with the LDS ring of the previous unit before it is refilled
+    wait_lgkmcnt0();
+    barrier();
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s, s);
+    wait_stages<LPS, STAGES - 1>(nk - 1);
+    barrier();
+    read_stage(0, std::integral_constant<int, 0>{});
+    wait_lgkmcnt0();
+
+    // one K block: register buffer `cur` holds stage i, stage i+1 goes to the other
+    auto step = [&](int i, auto cur_c) {
+      constexpr int cur = decltype(cur_c)::value;
+      if (i + 1 < nk) {
+        // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are pending
+        wait_stages<LPS, STAGES - 2>(nk - 2 - i);
+        barrier();
+        if (i + STAGES < nk) issue(i + STAGES, i % STAGES);
+        read_stage((i + 1) % STAGES, std::integral_constant<int, cur ^ 1>{});
+      }
+      compute(cur_c);
+      wait_lgkmcnt0();
+    };
+    for (int i = 0; i < nk; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < nk) step(i + 1, std::integral_constant<int, 1>{});
     }
 
-    // ---- split-K: publish the partial; the last of the S arrivals reduces in order
+    // ---- split-K: publish the partial with device-coherent stores; the last of the
+    // S arrivals reads the others (device-coherent loads) and reduces in split order
     if (S > 1) {
-      const int64_t tile_base = (int64_t)tile_id * S * (BM * BN);
+      float* tile_ws = p.ws + (int64_t)tile_id * S * (BM * BN);
       const int frag_base = (wave * TM * TN) * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          *reinterpret_cast<v4f*>(p.ws + tile_base + (int64_t)split * (BM * BN) +
-                                  (int64_t)(frag_base + (i * TN + j) * 64) * 4) = acc[i][j];
-      __threadfence();
+        for (int j = 0; j < TN; ++j) {
+          float* dst = tile_ws + (int64_t)split * (BM * BN) + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(dst + r, acc[t][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      wait_vmcnt<0>();  // the partial has reached the device-coherent level
       __syncthreads();
       if (tid == 0) {
-        const int old = atomicAdd(&p.counters[tile_id], 1);
+        const int old = __hip_atomic_fetch_add(&p.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_info = (old == S - 1);
       }
       __syncthreads();
       const int last = s_info;
       __syncthreads();
       if (!last) continue;
-      __threadfence();
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TM; ++t)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
           for (int q = 0; q < S; ++q) {
-            const v4f part = q == split ? acc[i][j]
-                : *reinterpret_cast<const v4f*>(p.ws + tile_base + (int64_t)q * (BM * BN) +
-                                                (int64_t)(frag_base + (i * TN + j) * 64) * 4);
+            v4f part;
+            if (q == split) {
+              part = acc[t][j];
+            } else {
+              const float* src = tile_ws + (int64_t)q * (BM * BN) + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                part[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             sum += part;
           }
-          acc[i][j] = sum;
+          acc[t][j] = sum;
         }
-      if (tid == 0) p.counters[tile_id] = 0;  // ready for the next call
+      if (tid == 0) __hip_atomic_store(&p.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue: BF16 round-to-nearest-even, live rows only
@@ -348,8 +455,8 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
     int live_rows = p.M;
     if (p.kind == kMasked) live_rows = min(max(p.masked_m[g], 0), p.M);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WTM + 16 * i + (lane & 15);
+    for (int t = 0; t < TM; ++t) {
+      const int m = m0 + wm * WTM + 16 * t + (lane & 15);
       bool ok = m < live_rows;
       if (ok && p.kind == kContiguous) ok = p.m_indices[m] >= 0;
       if (!ok) continue;
@@ -357,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * WTN + 16 * j + 4 * (lane >> 4);
-        const v4f v = acc[i][j];
+        const v4f v = acc[t][j];
         if (p.vec_store && n + 3 < p.N) {
           const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
           const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);

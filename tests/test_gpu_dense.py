@@ -122,3 +122,27 @@ def test_strided_operands(cuda_device):
     ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
     compare("normal", bits_of(Dbig)[:, :N], ref, "strided")
     assert np.all(bits_of(Dbig)[:, N:] == SENT), "columns beyond N must not be written"
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(64, 2112, 7168, None), (128, 4096, 7168, None), (100, 384, 2048, (64, 64, 8)),
+                                        (256, 640, 4096, (128, 128, 5))])
+def test_split_k_workspace_reuse_with_new_inputs(cuda_device, M, N, K, tile):
+    # a reduction that read a partial left from the previous call would pass a
+    # same-input determinism test; here every call has different operands
+    nbytes = fg.workspace_size(fg.KIND_DENSE, M, N, K)
+    if tile is not None:
+        t = fg.num_tiles(M, N, tile[0], tile[1])
+        nbytes = t * tile[2] * tile[0] * tile[1] * 4 + t * 4
+    work = torch.zeros(nbytes, dtype=torch.uint8, device=cuda_device)
+    rows = sample_rows(M, 10, K)
+    for call in range(3):
+        c = synth.dense_case(M, N, K, seed=600 + call, device=cuda_device, kind="e1" if call == 1 else "normal")
+        D = c["D"].clone()
+        if tile is None:
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+        else:
+            with fg.force_config(*tile):
+                fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+        torch.cuda.synchronize()
+        ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))
+        compare("e1" if call == 1 else "normal", bits_of(D)[rows], ref, f"call {call} {M}x{N}x{K}")
