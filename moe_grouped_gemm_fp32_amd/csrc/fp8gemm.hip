@@ -79,13 +79,15 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-// Compiled variants: tile shape, wave layout and LDS ring depth. Every variant
-// uses about 140 KB of LDS, so one workgroup runs per CU.
+// Compiled variants: tile shape, wave layout (4 or 8 wave64s) and LDS ring depth.
+// Every variant uses 136-158 KB of LDS, so one workgroup runs per CU.
 struct Variant {
   int bm, bn, waves_m, waves_n, stages;
 };
 constexpr Variant kVariants[] = {
-    {64, 64, 2, 2, 8}, {128, 64, 2, 2, 6}, {64, 128, 2, 2, 6}, {128, 128, 2, 2, 4}};
+    {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},
+    {128, 128, 2, 2, 4}, {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kOccupancy = 1;
 
 bool has_kernel(int bm, int bn) {
@@ -155,18 +157,20 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   return pl;
 }
 
-template <int I>
+template <int I, bool MASKED>
 hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
   constexpr Variant v = kVariants[I];
-  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, kOccupancy>),
-                     dim3(grid), dim3(fp8gemm::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED>), dim3(grid),
+                     dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int I = 0>
 hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream) {
-  if constexpr (I < (int)(sizeof(kVariants) / sizeof(kVariants[0]))) {
-    if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn) return launch_variant<I>(p, pl.grid, stream);
+  if constexpr (I < kNumVariants) {
+    if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn)
+      return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true>(p, pl.grid, stream)
+                                           : launch_variant<I, false>(p, pl.grid, stream);
     return launch<I + 1>(pl, p, stream);
   } else {
     return hipErrorInvalidValue;

@@ -33,7 +33,6 @@
 namespace fp8gemm {
 
 constexpr int kBlockK = 128;   // K extent of a scale block and of one MFMA
-constexpr int kThreads = 256;  // 4 wave64s per workgroup
 constexpr int kMaxGroups = 1024;
 constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 
@@ -95,26 +94,43 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int gm, 
   tn = r / gs;
 }
 
-// Byte offset of 16-byte chunk `c` (0..7) of LDS row `row` (128 bytes per row):
-// chunk c is stored at position c ^ (row & 7) so the 16 rows a fragment read
-// touches spread over all bank groups.
-__device__ __forceinline__ int swz(int row, int c) { return row * kBlockK + ((c ^ (row & 7)) << 4); }
+// LDS layout of a 128-byte operand row: 16-byte chunk c of row `row` is stored at
+// chunk position c ^ swz_key(row). gfx950's LDS has 64 four-byte banks (256 bytes),
+// i.e. two rows share one bank row; a fragment read has 16 lanes fetch the same
+// logical chunk of 16 consecutive rows, and the key (row >> 1) & 7 gives those 16
+// reads 16 distinct 16-byte bank groups (no conflicts).
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int c) { return row * kBlockK + ((c ^ swz_key(row)) << 4); }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima). The s_waitcnt builtin
+// orders nothing for the compiler, so every wait sits between scheduling barriers
+// (no instruction moves across) and memory clobbers: work written before the wait
+// in source order executes before it, work written after it executes after it.
+__device__ __forceinline__ void fence_schedule() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  fence_schedule();
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  fence_schedule();
 }
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  fence_schedule();
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+  fence_schedule();
+}
 
 // Workgroup barrier without the memory fence of __syncthreads (which would drain
 // every outstanding load); the empty asm keeps the compiler from moving LDS
 // accesses across it.
 __device__ __forceinline__ void barrier() {
+  fence_schedule();
   __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  fence_schedule();
 }
 
 // 32-bit LDS byte address of a __shared__ object.
@@ -146,29 +162,34 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OCC>
-__global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p) {
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+// BM x BN tile, WAVES_M x WAVES_N wave64s (4 or 8), STAGES-deep LDS ring; MASKED
+// instances carry the per-group live-tile table.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(const Params p) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int NT = NW * 64;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   constexpr int WTM = BM / WAVES_M;  // wave tile rows
   constexpr int WTN = BN / WAVES_N;  // wave tile cols
   constexpr int TM = WTM / 16;
   constexpr int TN = WTN / 16;
   static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   static_assert(kBlockK % WTN == 0, "a wave's columns must share one 128-column scale block");
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && BM <= 128, "tile load split");
+  static_assert((BM * kBlockK) % (1024 * NW) == 0 && (BN * kBlockK) % (1024 * NW) == 0, "tile load split");
   static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
   constexpr int B_BYTES = BN * kBlockK;
-  constexpr int SC_FLOATS = 4 * 64;                 // per stage: 64 scale slots per wave
+  constexpr int SC_FLOATS = NW * 64;                // per stage: 64 scale slots per wave
   constexpr int STAGE = A_BYTES + B_BYTES + SC_FLOATS * 4;
-  constexpr int A_INSTR = BM / 32;                  // 1 KB direct-to-LDS loads per wave per stage
-  constexpr int B_INSTR = BN / 32;
+  constexpr int A_INSTR = A_BYTES / (1024 * NW);    // 1 KB direct-to-LDS loads per wave per stage
+  constexpr int B_INSTR = B_BYTES / (1024 * NW);
   constexpr int LPS = A_INSTR + B_INSTR + 1;        // + one scale load
-  constexpr int SA_PER_WAVE = BM / 4;               // activation scales loaded by each wave
+  constexpr int SA_PER_WAVE = BM / NW;              // activation scales loaded by each wave
+  static_assert(SA_PER_WAVE >= 1 && SA_PER_WAVE <= 63, "scale slots");
   static_assert(LPS * (STAGES - 1) < 64, "vmcnt capacity");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE];
-  __shared__ int s_pre[kMaxGroups + 1];  // masked: prefix sums of live m-tiles per group
+  __shared__ int s_pre[MASKED ? kMaxGroups + 1 : 1];  // masked: prefix sums of live m-tiles per group
   __shared__ int s_info;
 
   const int tid = threadIdx.x;
@@ -180,8 +201,8 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
 
   // ---- masked: live m-tiles per group, exclusive prefix sum in LDS
   int num_units = p.num_units;
-  if (p.kind == kMasked) {
-    constexpr int PER = (kMaxGroups + kThreads - 1) / kThreads;
+  if constexpr (MASKED) {
+    constexpr int PER = (kMaxGroups + NT - 1) / NT;
     int local[PER];
     int run = 0;
     for (int q = 0; q < PER; ++q) {
@@ -194,10 +215,10 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
       local[q] = run;
       run += t;
     }
-    __shared__ int s_scan[kThreads];
+    __shared__ int s_scan[NT];
     s_scan[tid] = run;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
       const int v = tid >= off ? s_scan[tid - off] : 0;
       __syncthreads();
       s_scan[tid] += v;
@@ -208,7 +229,7 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
       const int g = tid * PER + q;
       if (g <= p.G && g < kMaxGroups + 1) s_pre[g] = base + local[q];
     }
-    if (tid == kThreads - 1) s_pre[min(p.G, kMaxGroups)] = s_scan[kThreads - 1];
+    if (tid == NT - 1) s_pre[min(p.G, kMaxGroups)] = s_scan[NT - 1];
     __syncthreads();
     num_units = s_pre[p.G] * p.tiles_n * S;
   }
@@ -216,7 +237,7 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
   for (int u = blockIdx.x; u < num_units; u += gridDim.x) {
     const int L = xcd_remap(u, num_units);
     int g = 0, tm, tn, split, tile_id;
-    if (p.kind == kMasked) {
+    if constexpr (MASKED) {
       // units of one (group, n-tile) are contiguous: the group's B tile is reused
       int lo = 0, hi = p.G;  // largest g with s_pre[g] * tiles_n * S <= L
       while (hi - lo > 1) {
@@ -256,28 +277,27 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
 
     const int kb0 = split * p.kb_per_split;
     const int nk = min(p.num_kb, kb0 + p.kb_per_split) - kb0;
-    const uint8_t* Ag = p.A + (p.kind == kMasked ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK;
-    const float* sag = p.sa + (p.kind == kMasked ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa;
+    const uint8_t* Ag = p.A + (MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK;
+    const float* sag = p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa;
     const uint8_t* Bg = p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK;
     const float* sbg = p.sb + (int64_t)g * p.sb_gstride + kb0;
 
     // ---- direct-to-LDS load plan. Load instruction r of this wave fills 8 rows
-    // (1 KB) of a stage: lane l brings row 8*grp + l/8, logical chunk
-    // (l & 7) ^ (l >> 3), i.e. LDS chunk l & 7 of that row (the swizzle above).
+    // (1 KB) of a stage: lane l writes chunk position l & 7 of row 8*grp + l/8, so it
+    // brings the logical chunk (l & 7) ^ swz_key(row) (the layout above).
     const int lrow = lane >> 3;
-    const int lchunk = ((lane & 7) ^ lrow) << 4;
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int r = 0; r < A_INSTR; ++r) {
-      const int row = (r * 4 + wave) * 8 + lrow;
+      const int row = (r * NW + wave) * 8 + lrow;
       const int grow = min(m0 + row, p.M - 1);  // rows past the end: clamped, results unused
-      a_off[r] = (uint32_t)(grow * p.lda) + lchunk;
+      a_off[r] = (uint32_t)(grow * p.lda) + (((lane & 7) ^ swz_key(row)) << 4);
     }
 #pragma unroll
     for (int r = 0; r < B_INSTR; ++r) {
-      const int row = (r * 4 + wave) * 8 + lrow;
+      const int row = (r * NW + wave) * 8 + lrow;
       const int grow = min(n0 + row, p.N - 1);
-      b_off[r] = (uint32_t)(grow * p.ldb) + lchunk;
+      b_off[r] = (uint32_t)(grow * p.ldb) + (((lane & 7) ^ swz_key(row)) << 4);
     }
     // scale load: lanes [0, BM/4) bring activation scales of rows wave*BM/4 + lane,
     // lane 63 brings this wave's weight scale, other lanes repeat lane 0's address
@@ -298,10 +318,10 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
       const uint32_t base = ring + stage * STAGE;
 #pragma unroll
       for (int r = 0; r < A_INSTR; ++r)
-        dma16(Ag + (int64_t)i * kBlockK + a_off[r], base + (r * 4 + wave) * 1024);
+        dma16(Ag + (int64_t)i * kBlockK + a_off[r], base + (r * NW + wave) * 1024);
 #pragma unroll
       for (int r = 0; r < B_INSTR; ++r)
-        dma16(Bg + (int64_t)i * kBlockK + b_off[r], base + A_BYTES + (r * 4 + wave) * 1024);
+        dma16(Bg + (int64_t)i * kBlockK + b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
       dma4(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256);
     };
 
@@ -320,8 +340,9 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
       sa_slot[t] = (row / SA_PER_WAVE) * 64 + row % SA_PER_WAVE;
     }
     // fragments and scales of one stage, read from LDS into registers
-    v8i fa[2][TM], fb[2][TN];
-    float sc[2][TM];
+    constexpr int NBUF = NW == 4 ? 2 : 1;
+    v8i fa[NBUF][TM], fb[NBUF][TN];
+    float sa_r[NBUF][TM], sb_r[NBUF];  // raw scales; multiplied only once the stage is consumed
     auto read_stage = [&](int stage, auto buf_c) {
       constexpr int buf = decltype(buf_c)::value;
       const uint8_t* sA = smem + stage * STAGE;
@@ -341,14 +362,17 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
         const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
         fb[buf][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      const float sbv = sS[wave * 64 + 63];
+      sb_r[buf] = sS[wave * 64 + 63];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) sc[buf][t] = sS[sa_slot[t]] * sbv;
+      for (int t = 0; t < TM; ++t) sa_r[buf][t] = sS[sa_slot[t]];
     };
     // one K block from registers: MFMAs in batches of TN (one A subtile), each
     // batch's promotion FMAs issued behind the next batch's MFMAs
     auto compute = [&](auto buf_c) {
       constexpr int buf = decltype(buf_c)::value;
+      float sc[TM];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) sc[t] = sa_r[buf][t] * sb_r[buf];
       v4f r[2][TN];
 #pragma unroll
       for (int t = 0; t <= TM; ++t) {
@@ -362,46 +386,61 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
           const int q = t - 1;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            acc[q][j][0] = __builtin_fmaf(r[q & 1][j][0], sc[buf][q], acc[q][j][0]);
-            acc[q][j][1] = __builtin_fmaf(r[q & 1][j][1], sc[buf][q], acc[q][j][1]);
-            acc[q][j][2] = __builtin_fmaf(r[q & 1][j][2], sc[buf][q], acc[q][j][2]);
-            acc[q][j][3] = __builtin_fmaf(r[q & 1][j][3], sc[buf][q], acc[q][j][3]);
+            acc[q][j][0] = __builtin_fmaf(r[q & 1][j][0], sc[q], acc[q][j][0]);
+            acc[q][j][1] = __builtin_fmaf(r[q & 1][j][1], sc[q], acc[q][j][1]);
+            acc[q][j][2] = __builtin_fmaf(r[q & 1][j][2], sc[q], acc[q][j][2]);
+            acc[q][j][3] = __builtin_fmaf(r[q & 1][j][3], sc[q], acc[q][j][3]);
           }
         }
       }
     };
 
-    // Ring schedule: stage i lives in slot i % STAGES. Before computing stage i
-    // (from registers) the wave reads stage i+1 into its other register buffer, and
-    // the slot of stage i (already in registers everywhere) is refilled with
-    // stage i + STAGES.
     // all waves are done with the LDS ring of the previous unit before it is refilled
     wait_lgkmcnt0();
     barrier();
+    if constexpr (NW == 4) {
+      // One wave per SIMD: fragments double-buffered in registers. Stage i lives in
+      // slot i % STAGES; before computing stage i (from registers) the wave reads
+      // stage i+1 into its other buffer, and the slot of stage i (already in
+      // registers everywhere) is refilled with stage i + STAGES.
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < nk) issue(s, s);
-    wait_stages<LPS, STAGES - 1>(nk - 1);
-    barrier();
-    read_stage(0, std::integral_constant<int, 0>{});
-    wait_lgkmcnt0();
-
-    // one K block: register buffer `cur` holds stage i, stage i+1 goes to the other
-    auto step = [&](int i, auto cur_c) {
-      constexpr int cur = decltype(cur_c)::value;
-      if (i + 1 < nk) {
-        // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are pending
-        wait_stages<LPS, STAGES - 2>(nk - 2 - i);
-        barrier();
-        if (i + STAGES < nk) issue(i + STAGES, i % STAGES);
-        read_stage((i + 1) % STAGES, std::integral_constant<int, cur ^ 1>{});
-      }
-      compute(cur_c);
+      for (int s = 0; s < STAGES; ++s)
+        if (s < nk) issue(s, s);
+      wait_stages<LPS, STAGES - 1>(nk - 1);
+      barrier();
+      read_stage(0, std::integral_constant<int, 0>{});
       wait_lgkmcnt0();
-    };
-    for (int i = 0; i < nk; i += 2) {
-      step(i, std::integral_constant<int, 0>{});
-      if (i + 1 < nk) step(i + 1, std::integral_constant<int, 1>{});
+      auto step = [&](int i, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        if (i + 1 < nk) {
+          // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are pending
+          wait_stages<LPS, STAGES - 2>(nk - 2 - i);
+          barrier();
+          if (i + STAGES < nk) issue(i + STAGES, i % STAGES);
+          read_stage((i + 1) % STAGES, std::integral_constant<int, cur ^ 1>{});
+        }
+        compute(cur_c);
+        wait_lgkmcnt0();
+      };
+      for (int i = 0; i < nk; i += 2) {
+        step(i, std::integral_constant<int, 0>{});
+        if (i + 1 < nk) step(i + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      // Two waves per SIMD: one register buffer; the SIMD's other wave computes
+      // while this one reads. Stage i lives in slot i % STAGES and refills the slot
+      // of stage i-1, which every wave has consumed once past the barrier.
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+      for (int i = 0; i < nk; ++i) {
+        wait_stages<LPS, STAGES - 2>(nk - 1 - i);
+        barrier();
+        if (i + STAGES - 1 < nk) issue(i + STAGES - 1, (i + STAGES - 1) % STAGES);
+        read_stage(i % STAGES, std::integral_constant<int, 0>{});
+        wait_lgkmcnt0();
+        compute(std::integral_constant<int, 0>{});
+      }
     }
 
     // ---- split-K: publish the partial with device-coherent stores; the last of the
@@ -451,9 +490,9 @@ __global__ void __launch_bounds__(kThreads, OCC) fp8_gemm_kernel(const Params p)
     }
 
     // ---- epilogue: BF16 round-to-nearest-even, live rows only
-    uint16_t* Dg = p.D + (p.kind == kMasked ? (int64_t)g * p.d_gstride : 0);
+    uint16_t* Dg = p.D + (MASKED ? (int64_t)g * p.d_gstride : 0);
     int live_rows = p.M;
-    if (p.kind == kMasked) live_rows = min(max(p.masked_m[g], 0), p.M);
+    if (MASKED) live_rows = min(max(p.masked_m[g], 0), p.M);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int m = m0 + wm * WTM + 16 * t + (lane & 15);

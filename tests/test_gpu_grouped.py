@@ -47,7 +47,8 @@ def d_bits(c):
 
 
 @pytest.mark.parametrize("kind", ["normal", "e1", "e3"])
-@pytest.mark.parametrize("tile", [None, (64, 64, 1), (128, 128, 1), (64, 128, 1), (128, 64, 1), (64, 64, 2)],
+@pytest.mark.parametrize("tile", [None, (64, 64, 1), (128, 128, 1), (64, 128, 1), (128, 64, 1), (64, 64, 2),
+                                  (128, 256, 1), (128, 256, 2)],
                          ids=lambda t: "auto" if t is None else "%dx%d_s%d" % t)
 def test_contiguous_small_all_tiles(cuda_device, kind, tile):
     c = synth.contiguous_case([5, 128, 0, 130, 1, 300], 200, 384, seed=41, device=cuda_device, kind=kind)
@@ -81,7 +82,7 @@ def test_contiguous_all_padding_block_and_dense_equivalence(cuda_device):
 
 
 @pytest.mark.parametrize("kind", ["normal", "e1", "e2"])
-@pytest.mark.parametrize("tile", [None, (64, 64, 1), (64, 128, 1), (128, 128, 1)],
+@pytest.mark.parametrize("tile", [None, (64, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1)],
                          ids=lambda t: "auto" if t is None else "%dx%d_s%d" % t)
 def test_masked_small_all_tiles(cuda_device, kind, tile):
     c = synth.masked_case(5, 256, 160, 384, seed=51, device=cuda_device, masked_m=[256, 0, 1, 179, 64],
