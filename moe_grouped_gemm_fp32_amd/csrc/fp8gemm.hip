@@ -85,8 +85,8 @@ struct Variant {
   int bm, bn, waves_m, waves_n, stages;
 };
 constexpr Variant kVariants[] = {
-    {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},
-    {128, 128, 2, 2, 4}, {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}};
+    {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},  {128, 128, 2, 2, 4},
+    {256, 128, 2, 2, 3}, {128, 256, 2, 2, 3}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kOccupancy = 1;
 
@@ -101,9 +101,26 @@ size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
   return (size_t)tiles * split * bm * bn * sizeof(float) + (size_t)tiles * sizeof(int32_t);
 }
 
+// Cost model of the planner (microseconds, measured on MI355X): time of one
+// 128-wide K block of one work unit per tile variant, the fixed cost of a work unit
+// (pipeline fill and epilogue) and the extra cost of a split-K unit (publishing its
+// partial, plus the last arrival reading the other partials). A call's estimate is
+// rounds * (unit cost) with rounds = ceil(units / CUs), so the planner trades tile
+// efficiency against filling all CUs (the unaligned-block argument of the pages:
+// deepep.org/zh/deepgemm, 非对齐块大小).
+constexpr double kUnitFixedUs = 5.0;
+constexpr double kSplitUnitUs = 6.0;
+constexpr double kSplitReadUsPerKB = 0.125;
+constexpr int kMaxSplit = 8;
+double kb_cost_us(int bm, int bn) {
+  if (bm == 64 && bn == 64) return 0.45;
+  if (bm == 128 && bn == 128) return 0.67;
+  if (bm * bn == 128 * 64) return 0.60;
+  return 1.60;  // 256x128 / 128x256
+}
+
 // Choose tile shape and split for a call. `rows` is M (dense), M_total
-// (contiguous) or expected live rows per group (masked); `groups` multiplies the
-// m-tile count for masked.
+// (contiguous) or M_max (masked, where expected_m estimates the live rows).
 Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
   Plan pl;
   const int num_kb = K / fp8gemm::kBlockK;
@@ -112,29 +129,31 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     pl.bn = g_forced_cfg.block_n;
     pl.split = std::max(1, g_forced_cfg.split_k);
   } else {
-    int bm, bn;
-    if (kind == FP8GEMM_KIND_MASKED) {
-      const int live = std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows));
-      bm = 64;
-      const int64_t t128 = (int64_t)G * ceil_div(live, bm) * ceil_div(N, 128);
-      bn = t128 >= cus ? 128 : 64;
-    } else if (rows <= 64) {
-      bm = 64; bn = 64;
-    } else if (rows <= 128) {
-      bm = 128; bn = 64;
-    } else {
-      bm = 128; bn = 128;
-      if (ceil_div(rows, bm) * ceil_div(N, bn) < cus) bn = 64;
-    }
-    pl.bm = bm;
-    pl.bn = bn;
-    pl.split = 1;
-    if (kind != FP8GEMM_KIND_MASKED) {
-      const int64_t tiles = ceil_div(rows, bm) * ceil_div(N, bn);
-      if (tiles < cus && num_kb >= 4) {
-        int want = (int)std::min<int64_t>(ceil_div(cus, tiles), num_kb / 2);
-        want = std::max(1, want);
-        pl.split = want;
+    double best = 1e30;
+    const int live = kind == FP8GEMM_KIND_MASKED ? std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows))
+                                                 : rows;
+    for (const auto& v : kVariants) {
+      if (kind == FP8GEMM_KIND_CONTIGUOUS && 128 % v.bm != 0) continue;  // one expert per tile
+      if (v.bm >= 2 * 128 && live <= 128) continue;                      // mostly empty tiles
+      const int64_t tiles =
+          ceil_div(live, v.bm) * ceil_div(N, v.bn) * (kind == FP8GEMM_KIND_MASKED ? G : 1);
+      const int max_split = kind == FP8GEMM_KIND_MASKED ? 1 : std::min(num_kb, kMaxSplit);
+      for (int sp = 1; sp <= max_split; ++sp) {
+        const int kbps = (int)ceil_div(num_kb, sp);
+        const int split = (int)ceil_div(num_kb, kbps);
+        if (split != sp) continue;  // same as a smaller split
+        if (split > 1 && split_ws_bytes(ceil_div(rows, v.bm) * ceil_div(N, v.bn), split, v.bm, v.bn) > ws_avail)
+          continue;
+        const int64_t rounds = ceil_div(tiles * split, cus);
+        const double reduce =
+            split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
+        const double t = (double)rounds * (kUnitFixedUs + kbps * kb_cost_us(v.bm, v.bn) + reduce);
+        if (t < best * 0.999) {
+          best = t;
+          pl.bm = v.bm;
+          pl.bn = v.bn;
+          pl.split = split;
+        }
       }
     }
   }

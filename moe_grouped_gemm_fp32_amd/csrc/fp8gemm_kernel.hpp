@@ -179,13 +179,17 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
   constexpr int B_BYTES = BN * kBlockK;
-  constexpr int SC_FLOATS = NW * 64;                // per stage: 64 scale slots per wave
+  constexpr int SA_PER_WAVE = BM / NW;              // activation scales loaded by each wave
+  static_assert(SA_PER_WAVE >= 1 && SA_PER_WAVE <= 64, "scale slots");
+  // scale loads per wave per stage: one when the weight scale fits in lane 63 of the
+  // activation-scale load, else a second one for it
+  constexpr int SC_INSTR = SA_PER_WAVE < 64 ? 1 : 2;
+  constexpr int SC_FLOATS = NW * 64 * SC_INSTR;     // per stage: 64 scale slots per wave per load
   constexpr int STAGE = A_BYTES + B_BYTES + SC_FLOATS * 4;
   constexpr int A_INSTR = A_BYTES / (1024 * NW);    // 1 KB direct-to-LDS loads per wave per stage
   constexpr int B_INSTR = B_BYTES / (1024 * NW);
-  constexpr int LPS = A_INSTR + B_INSTR + 1;        // + one scale load
-  constexpr int SA_PER_WAVE = BM / NW;              // activation scales loaded by each wave
-  static_assert(SA_PER_WAVE >= 1 && SA_PER_WAVE <= 63, "scale slots");
+  constexpr int LPS = A_INSTR + B_INSTR + SC_INSTR;
+  constexpr int SB_SLOT = SC_INSTR == 1 ? 63 : 64;  // weight scale of a wave within its scale slots
   static_assert(LPS * (STAGES - 1) < 64, "vmcnt capacity");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE];
@@ -299,30 +303,37 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       const int grow = min(n0 + row, p.N - 1);
       b_off[r] = (uint32_t)(grow * p.ldb) + (((lane & 7) ^ swz_key(row)) << 4);
     }
-    // scale load: lanes [0, BM/4) bring activation scales of rows wave*BM/4 + lane,
-    // lane 63 brings this wave's weight scale, other lanes repeat lane 0's address
+    // scale loads: lanes [0, BM/NW) bring activation scales of rows wave*BM/NW + lane
+    // and this wave's weight scale goes to slot SB_SLOT (lane 63 of the same load, or
+    // every lane of a second load); spare lanes repeat lane 0's address
+    const float* sb_src = sbg + (int64_t)(min(n0 + wn * WTN, p.N - 1) / kBlockK) * p.num_kb;
     const float* sc_src;
-    {
-      const int wave_col = min(n0 + wn * WTN, p.N - 1);
-      if (lane == 63) {
-        sc_src = sbg + (int64_t)(wave_col / kBlockK) * p.num_kb;
-      } else {
-        const int row = wave * SA_PER_WAVE + (lane < SA_PER_WAVE ? lane : 0);
-        sc_src = sag + min(m0 + row, p.M - 1);
-      }
+    if (SC_INSTR == 1 && lane == 63) {
+      sc_src = sb_src;
+    } else {
+      const int row = wave * SA_PER_WAVE + (lane < SA_PER_WAVE ? lane : 0);
+      sc_src = sag + min(m0 + row, p.M - 1);
     }
-    const int64_t sc_step = lane == 63 ? 1 : p.ld_sa;  // per K block
+    const int64_t sc_step = (SC_INSTR == 1 && lane == 63) ? 1 : p.ld_sa;  // per K block
 
     const uint32_t ring = lds_addr(smem);
-    auto issue = [&](int i, int stage) {  // load K block kb0 + i into `stage`
+    // load item q (0 <= q < LPS) of K block kb0 + i into `stage`: A rows, B rows, scales
+    auto issue_item = [&](int i, int stage, int q) {
       const uint32_t base = ring + stage * STAGE;
-#pragma unroll
-      for (int r = 0; r < A_INSTR; ++r)
-        dma16(Ag + (int64_t)i * kBlockK + a_off[r], base + (r * NW + wave) * 1024);
-#pragma unroll
-      for (int r = 0; r < B_INSTR; ++r)
+      if (q < A_INSTR) {
+        dma16(Ag + (int64_t)i * kBlockK + a_off[q], base + (q * NW + wave) * 1024);
+      } else if (q < A_INSTR + B_INSTR) {
+        const int r = q - A_INSTR;
         dma16(Bg + (int64_t)i * kBlockK + b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
-      dma4(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256);
+      } else if (q == A_INSTR + B_INSTR) {
+        dma4(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR);
+      } else {
+        dma4(sb_src + i, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR + 256);
+      }
+    };
+    auto issue = [&](int i, int stage) {
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) issue_item(i, stage, q);
     };
 
     v4f acc[TM][TN];
@@ -337,70 +348,87 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int row = wm * WTM + 16 * t + frow;
-      sa_slot[t] = (row / SA_PER_WAVE) * 64 + row % SA_PER_WAVE;
+      sa_slot[t] = (row / SA_PER_WAVE) * 64 * SC_INSTR + row % SA_PER_WAVE;
     }
-    // fragments and scales of one stage, read from LDS into registers
-    constexpr int NBUF = NW == 4 ? 2 : 1;
+    // fragments and scales of one stage, read from LDS into registers. Read item q:
+    // B fragments first, then the scales, then the A fragments, so a compute that
+    // starts before all reads have landed needs only the oldest ones.
+    // Double-buffered fragments only where the registers allow it (4 waves with
+    // wave tiles up to 64x64); otherwise one buffer read just before its compute.
+    constexpr bool DB = NW == 4 && TM * TN <= 16;
+    constexpr int NBUF = DB ? 2 : 1;
+    constexpr int NREAD = TN + 1 + TM;
     v8i fa[NBUF][TM], fb[NBUF][TN];
     float sa_r[NBUF][TM], sb_r[NBUF];  // raw scales; multiplied only once the stage is consumed
-    auto read_stage = [&](int stage, auto buf_c) {
+    auto read_item = [&](int stage, auto buf_c, int q) {
       constexpr int buf = decltype(buf_c)::value;
       const uint8_t* sA = smem + stage * STAGE;
       const uint8_t* sB = sA + A_BYTES;
       const float* sS = reinterpret_cast<const float*>(sB + B_BYTES);
+      if (q < TN) {
+        const int row = wn * WTN + 16 * q + frow;
+        const v4i lo = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk));
+        const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
+        fb[buf][q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else if (q == TN) {
+        sb_r[buf] = sS[wave * 64 * SC_INSTR + SB_SLOT];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
+        for (int t = 0; t < TM; ++t) sa_r[buf][t] = sS[sa_slot[t]];
+      } else {
+        const int t = q - TN - 1;
         const int row = wm * WTM + 16 * t + frow;
         const v4i lo = *reinterpret_cast<const v4i*>(sA + swz(row, fchunk));
         const v4i hi = *reinterpret_cast<const v4i*>(sA + swz(row, fchunk + 1));
         fa[buf][t] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WTN + 16 * j + frow;
-        const v4i lo = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk));
-        const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
-        fb[buf][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      sb_r[buf] = sS[wave * 64 + 63];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) sa_r[buf][t] = sS[sa_slot[t]];
     };
-    // one K block from registers: MFMAs in batches of TN (one A subtile), each
-    // batch's promotion FMAs issued behind the next batch's MFMAs
-    auto compute = [&](auto buf_c) {
+    auto read_stage = [&](int stage, auto buf_c) {
+#pragma unroll
+      for (int q = 0; q < NREAD; ++q) read_item(stage, buf_c, q);
+    };
+    // One K block from registers, as TM*TN slots. Slot k issues MFMA k (A subtile
+    // k / TN, B subtile k % TN), then `side(k)` (this slot's share of the global and
+    // LDS traffic of the iteration), then the promotion FMAs of MFMA k-2, whose
+    // result is ready by then. Scheduling barriers keep the slots in this order so
+    // the load traffic runs in the matrix unit's shadow.
+    constexpr int NMF = TM * TN;
+    auto compute = [&](auto buf_c, auto&& side) {
       constexpr int buf = decltype(buf_c)::value;
       float sc[TM];
 #pragma unroll
       for (int t = 0; t < TM; ++t) sc[t] = sa_r[buf][t] * sb_r[buf];
-      v4f r[2][TN];
+      v4f r[NMF];
+      auto promote = [&](int k) {
+        const int t = k / TN, j = k % TN;
+        const v4f v = r[k];
+        acc[t][j][0] = __builtin_fmaf(v[0], sc[t], acc[t][j][0]);
+        acc[t][j][1] = __builtin_fmaf(v[1], sc[t], acc[t][j][1]);
+        acc[t][j][2] = __builtin_fmaf(v[2], sc[t], acc[t][j][2]);
+        acc[t][j][3] = __builtin_fmaf(v[3], sc[t], acc[t][j][3]);
+      };
 #pragma unroll
-      for (int t = 0; t <= TM; ++t) {
-        if (t < TM) {
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            r[t & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                fb[buf][j], fa[buf][t], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        }
-        if (t > 0) {
-          const int q = t - 1;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            acc[q][j][0] = __builtin_fmaf(r[q & 1][j][0], sc[q], acc[q][j][0]);
-            acc[q][j][1] = __builtin_fmaf(r[q & 1][j][1], sc[q], acc[q][j][1]);
-            acc[q][j][2] = __builtin_fmaf(r[q & 1][j][2], sc[q], acc[q][j][2]);
-            acc[q][j][3] = __builtin_fmaf(r[q & 1][j][3], sc[q], acc[q][j][3]);
-          }
-        }
+      for (int k = 0; k < NMF; ++k) {
+        r[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            fb[buf][k % TN], fa[buf][k / TN], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        side(k);
+        if (k >= 2) promote(k - 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (NMF >= 2) promote(NMF - 2);
+      promote(NMF - 1);
+    };
+    // slot k of NMF gets items [k*n/NMF, (k+1)*n/NMF) of a list of n
+    auto share = [](int k, int n, auto&& f) {
+#pragma unroll
+      for (int q = k * n / NMF; q < (k + 1) * n / NMF; ++q) f(q);
     };
 
     // all waves are done with the LDS ring of the previous unit before it is refilled
     wait_lgkmcnt0();
     barrier();
-    if constexpr (NW == 4) {
-      // One wave per SIMD: fragments double-buffered in registers. Stage i lives in
-      // slot i % STAGES; before computing stage i (from registers) the wave reads
+    if constexpr (DB) {
+      // Fragments double-buffered in registers. Stage i lives in
+      // slot i % STAGES; while computing stage i (from registers) the wave reads
       // stage i+1 into its other buffer, and the slot of stage i (already in
       // registers everywhere) is refilled with stage i + STAGES.
 #pragma unroll
@@ -410,36 +438,57 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       barrier();
       read_stage(0, std::integral_constant<int, 0>{});
       wait_lgkmcnt0();
-      auto step = [&](int i, auto cur_c) {
-        constexpr int cur = decltype(cur_c)::value;
-        if (i + 1 < nk) {
+      // MORE: stage i+1 exists (read it); REFILL: stage i+STAGES exists (load it)
+      auto step_body = [&](int i, auto cur_c, auto more_c, auto refill_c) {
+        constexpr int nxt = decltype(cur_c)::value ^ 1;
+        constexpr bool MORE = decltype(more_c)::value;
+        constexpr bool REFILL = decltype(refill_c)::value;
+        if constexpr (MORE) {
           // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are pending
           wait_stages<LPS, STAGES - 2>(nk - 2 - i);
           barrier();
-          if (i + STAGES < nk) issue(i + STAGES, i % STAGES);
-          read_stage((i + 1) % STAGES, std::integral_constant<int, cur ^ 1>{});
         }
-        compute(cur_c);
+        const int rs = (i + 1) % STAGES, ws = i % STAGES;
+        compute(cur_c, [&](int k) {
+          if constexpr (REFILL) share(k, LPS, [&](int q) { issue_item(i + STAGES, ws, q); });
+          if constexpr (MORE) share(k, NREAD, [&](int q) { read_item(rs, std::integral_constant<int, nxt>{}, q); });
+        });
         wait_lgkmcnt0();
+      };
+      auto step = [&](int i, auto cur_c) {
+        using T = std::true_type;
+        using F = std::false_type;
+        if (i + STAGES < nk) step_body(i, cur_c, T{}, T{});
+        else if (i + 1 < nk) step_body(i, cur_c, T{}, F{});
+        else step_body(i, cur_c, F{}, F{});
       };
       for (int i = 0; i < nk; i += 2) {
         step(i, std::integral_constant<int, 0>{});
         if (i + 1 < nk) step(i + 1, std::integral_constant<int, 1>{});
       }
     } else {
-      // Two waves per SIMD: one register buffer; the SIMD's other wave computes
-      // while this one reads. Stage i lives in slot i % STAGES and refills the slot
-      // of stage i-1, which every wave has consumed once past the barrier.
+      // One register buffer: the stage is read right before its compute (the
+      // compiler waits per MFMA batch for just the fragments it needs, and with two
+      // waves per SIMD the other wave computes meanwhile). Stage i lives in slot
+      // i % STAGES and refills the slot of stage i-1, which every wave has consumed
+      // once past the barrier.
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue(s, s);
-      for (int i = 0; i < nk; ++i) {
+      auto step_body = [&](int i, auto refill_c) {
+        constexpr bool REFILL = decltype(refill_c)::value;
         wait_stages<LPS, STAGES - 2>(nk - 1 - i);
         barrier();
-        if (i + STAGES - 1 < nk) issue(i + STAGES - 1, (i + STAGES - 1) % STAGES);
         read_stage(i % STAGES, std::integral_constant<int, 0>{});
+        const int ws = (i + STAGES - 1) % STAGES;
+        compute(std::integral_constant<int, 0>{}, [&](int k) {
+          if constexpr (REFILL) share(k, LPS, [&](int q) { issue_item(i + STAGES - 1, ws, q); });
+        });
         wait_lgkmcnt0();
-        compute(std::integral_constant<int, 0>{});
+      };
+      for (int i = 0; i < nk; ++i) {
+        if (i + STAGES - 1 < nk) step_body(i, std::true_type{});
+        else step_body(i, std::false_type{});
       }
     }
 

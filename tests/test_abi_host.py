@@ -99,9 +99,9 @@ def test_planner_invariants_on_dense_shapes(cus256, M, N, K):
     # every split owns at least one K block
     kbps = -(-nkb // s)
     assert kbps * (s - 1) < nkb
-    # small problems are spread over (at least nearly) all CUs
-    if tiles < 256:
-        assert cfg["num_units"] >= 224 or s == nkb // 2
+    # the planner does not leave most CUs idle when K allows splitting
+    if tiles < 64 and nkb >= 16:
+        assert s > 1 and cfg["num_units"] >= 128
     assert cfg["grid"] <= cfg["num_units"] and cfg["grid"] <= 512
     ws = fg.workspace_size(fg.KIND_DENSE, M, N, K)
     assert (ws > 0) == (s > 1)
@@ -115,7 +115,7 @@ def test_planner_masked_and_contiguous(cus256):
     for G in (1, 2, 4, 8, 16):
         for N, K in ((4096, 7168), (7168, 2048)):
             cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
-            assert cfg["split_k"] == 1 and 128 % cfg["block_m"] == 0
+            assert cfg["split_k"] == 1 and cfg["block_m"] in (64, 128, 256)
             assert fg.workspace_size(fg.KIND_MASKED, 4096, N, K, G, 256) == 0
     cfg = fg.query_config(fg.KIND_CONTIGUOUS, 32768, 4096, 7168, 4)
     assert 128 % cfg["block_m"] == 0
