@@ -13,6 +13,9 @@ reused within a step, so each GEMM streams its inputs from HBM). Prints one JSON
   cpu_baseline = the CPU oracle timed on one full shape on this host
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -40,6 +43,99 @@ def classify(flops, nbytes):
     t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     return ("mfma", t_mfma) if t_mfma >= t_hbm else ("hbm", t_hbm)
+
+
+def kernel_source_hash():
+    """sha256 of the HIP sources: counter-derived traffic is only valid for this kernel."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_fp32_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_csv(d, counter):
+    """Per-dispatch values of `counter` from a rocprofv3 --pmc csv directory: list of (kernel, value)."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def pmc_summary(args, shapes):
+    """Build the HBM-traffic table from FETCH_SIZE / WRITE_SIZE runs of this benchmark and of
+    the plain copy (--copy-mb). Counters are KiB per dispatch; each is scaled by the ratio
+    (known copy bytes) / (counter bytes of the copy)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
+    copy_bytes = args.copy_mb * (1 << 20)
+
+    def copy_factor(d, counter):
+        vals = [v for k, v in read_counter_csv(d, counter) if "fp8_gemm" not in k]
+        big = max(vals)  # the copy kernel moves the most bytes of its process
+        return copy_bytes / (big * 1024.0)
+
+    ff = copy_factor(cfetch_dir, "FETCH_SIZE")
+    fw = copy_factor(cwrite_dir, "WRITE_SIZE")
+    fetch = [v for k, v in read_counter_csv(fetch_dir, "FETCH_SIZE") if "fp8_gemm" in k]
+    write = [v for k, v in read_counter_csv(write_dir, "WRITE_SIZE") if "fp8_gemm" in k]
+    table = {}
+    for i, (M, N, K) in enumerate(shapes):
+        f = fetch[i::len(shapes)]
+        w = write[i::len(shapes)]
+        fk = sum(f) / len(f)
+        wk = sum(w) / len(w)
+        _, algo = algo_work(M, N, K)
+        traffic = fk * 1024.0 * ff + wk * 1024.0 * fw
+        table["%d,%d,%d" % (M, N, K)] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                         "bytes_per_launch": round(traffic), "algo_bytes": algo,
+                                         "traffic_over_algo": round(traffic / algo, 3)}
+    out = {"kernel_sha": kernel_source_hash(), "copy_mb": args.copy_mb, "fetch_factor": round(ff, 4),
+           "write_factor": round(fw, 4), "shapes": table}
+    with open(args.traffic_file, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def trace_summary(d, shapes):
+    """Per-shape average GEMM kernel duration from a rocprofv3 --kernel-trace csv directory
+    (dispatch i of the GEMM kernel belongs to shape i mod len(shapes))."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "fp8_gemm_kernel" in r["Kernel_Name"]:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    out = []
+    for i, (M, N, K) in enumerate(shapes):
+        sel = rows[i::len(shapes)]
+        us = sum(r[2] for r in sel) / len(sel) / 1e3
+        flops, nbytes = algo_work(M, N, K)
+        out.append({"M": M, "N": N, "K": K, "kernel": sel[0][1].replace("void fp8gemm::", ""),
+                    "dispatches": len(sel), "avg_us": round(us, 2),
+                    "tflops": round(flops / us / 1e6, 1), "gbs": round(nbytes / us / 1e3, 1)})
+    for o in out:
+        print(json.dumps(o))
+
+
+def copy_only(args):
+    """A plain device copy of --copy-mb MiB, the calibration kernel for the byte counters."""
+    import torch
+    n = args.copy_mb * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}))
 
 
 def parse_shapes(text):
@@ -88,8 +184,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_config2.json"))
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
+    ap.add_argument("--copy-mb", type=int, default=0, help="only run a plain copy of this many MiB")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR", help="per-shape durations from a rocprofv3 trace")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="build the traffic table from rocprofv3 --pmc output directories")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(args, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        return
+    if args.copy_mb:
+        copy_only(args)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported" % args.gpus}))
@@ -141,7 +251,9 @@ def main():
     traffic = {}
     if os.path.exists(args.traffic_file):
         with open(args.traffic_file) as f:
-            traffic = json.load(f)
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_source_hash():  # counters of this very kernel only
+            traffic = tr.get("shapes", {})
 
     total_flops = 0.0
     rows = []
