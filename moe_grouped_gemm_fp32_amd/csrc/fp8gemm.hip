@@ -86,7 +86,7 @@ struct Variant {
 };
 constexpr Variant kVariants[] = {
     {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},  {128, 128, 2, 2, 4},
-    {256, 128, 2, 2, 3}, {128, 256, 2, 2, 3}};
+    {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kOccupancy = 1;
 

@@ -138,17 +138,36 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Wave-uniform copies of values the compiler cannot prove uniform (a value read from
+// LDS, an index derived from threadIdx.x >> 6), so they and everything computed from
+// them live in scalar registers; a no-op on values already known to be uniform.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ const T* uni(const T* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Direct-to-LDS loads: every lane reads `bytes` from its own global address and the
 // wave writes them to LDS at m0 + lane * bytes. Issued as asm so the compiler does
 // not treat them as LDS stores it must drain before every LDS read; completion is
-// tracked by the caller's explicit vmcnt waits.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+// tracked by the caller's explicit vmcnt waits. The address is a wave-uniform base
+// in scalar registers plus a per-lane 32-bit byte offset, so advancing a K block
+// and setting m0 cost only scalar instructions.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
+}
+// per-lane 64-bit address (lanes reading from different arrays)
+__device__ __forceinline__ void dma4v(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+               :: "v"(src), "s"(uni((int)lds)) : "memory");
 }
 
 // Wait until at most min(n, MAXN) groups of LPS loads are outstanding.
@@ -198,7 +217,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int S = p.split_k;
@@ -248,14 +267,15 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         const int mid = (lo + hi) >> 1;
         if (s_pre[mid] * p.tiles_n * S <= L) lo = mid; else hi = mid;
       }
-      g = lo;
-      const int live_tiles = s_pre[g + 1] - s_pre[g];
-      const int local = L - s_pre[g] * p.tiles_n * S;
+      g = uni(lo);
+      const int pre = uni(s_pre[g]);
+      const int live_tiles = uni(s_pre[g + 1]) - pre;
+      const int local = L - pre * p.tiles_n * S;
       tn = local / (live_tiles * S);
       const int r = local - tn * live_tiles * S;
       tm = r / S;
       split = r - tm * S;
-      tile_id = (s_pre[g] + tm) * p.tiles_n + tn;
+      tile_id = (pre + tm) * p.tiles_n + tn;
     } else {
       const int tile = L / S;
       split = L - tile * S;
@@ -274,17 +294,17 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         if (e >= 0) atomicMax(&s_info, e);
       }
       __syncthreads();
-      g = s_info;
+      g = uni(s_info);
       __syncthreads();
       if (g < 0 || g >= p.G) continue;  // all padding (or an invalid id): nothing to write
     }
 
     const int kb0 = split * p.kb_per_split;
     const int nk = min(p.num_kb, kb0 + p.kb_per_split) - kb0;
-    const uint8_t* Ag = p.A + (MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK;
-    const float* sag = p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa;
-    const uint8_t* Bg = p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK;
-    const float* sbg = p.sb + (int64_t)g * p.sb_gstride + kb0;
+    const uint8_t* Ag = uni(p.A + (MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK);
+    const float* sag = uni(p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa);
+    const uint8_t* Bg = uni(p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK);
+    const float* sbg = uni(p.sb + (int64_t)g * p.sb_gstride + kb0);
 
     // ---- direct-to-LDS load plan. Load instruction r of this wave fills 8 rows
     // (1 KB) of a stage: lane l writes chunk position l & 7 of row 8*grp + l/8, so it
@@ -306,7 +326,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     // scale loads: lanes [0, BM/NW) bring activation scales of rows wave*BM/NW + lane
     // and this wave's weight scale goes to slot SB_SLOT (lane 63 of the same load, or
     // every lane of a second load); spare lanes repeat lane 0's address
-    const float* sb_src = sbg + (int64_t)(min(n0 + wn * WTN, p.N - 1) / kBlockK) * p.num_kb;
+    const float* sb_src = uni(sbg + (int64_t)(min(n0 + wn * WTN, p.N - 1) / kBlockK) * p.num_kb);
     const float* sc_src;
     if (SC_INSTR == 1 && lane == 63) {
       sc_src = sb_src;
@@ -321,14 +341,14 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     auto issue_item = [&](int i, int stage, int q) {
       const uint32_t base = ring + stage * STAGE;
       if (q < A_INSTR) {
-        dma16(Ag + (int64_t)i * kBlockK + a_off[q], base + (q * NW + wave) * 1024);
+        dma16(Ag + (int64_t)i * kBlockK, a_off[q], base + (q * NW + wave) * 1024);
       } else if (q < A_INSTR + B_INSTR) {
         const int r = q - A_INSTR;
-        dma16(Bg + (int64_t)i * kBlockK + b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
+        dma16(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
       } else if (q == A_INSTR + B_INSTR) {
-        dma4(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR);
+        dma4v(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR);
       } else {
-        dma4(sb_src + i, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR + 256);
+        dma4(sb_src + i, 0u, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR + 256);
       }
     };
     auto issue = [&](int i, int stage) {
@@ -438,14 +458,21 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       barrier();
       read_stage(0, std::integral_constant<int, 0>{});
       wait_lgkmcnt0();
-      // MORE: stage i+1 exists (read it); REFILL: stage i+STAGES exists (load it)
+      // MORE: stage i+1 exists (read it); REFILL: stage i+STAGES exists (load it).
+      // Every step is one basic block: its waits have compile-time counts and nothing
+      // in it branches. (Across a branch the compiler sinks a step's promotions, which
+      // keeps every MFMA result live, and where differently compiled steps join it
+      // copies the accumulators.)
       auto step_body = [&](int i, auto cur_c, auto more_c, auto refill_c) {
         constexpr int nxt = decltype(cur_c)::value ^ 1;
         constexpr bool MORE = decltype(more_c)::value;
         constexpr bool REFILL = decltype(refill_c)::value;
         if constexpr (MORE) {
-          // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are pending
-          wait_stages<LPS, STAGES - 2>(nk - 2 - i);
+          // stage i+1 is complete once at most min(STAGES-2, nk-2-i) later stages are
+          // pending; with REFILL that is STAGES-2. Without, all loads were issued at
+          // least STAGES-1 steps ago, so waiting for every one of them costs little.
+          if constexpr (REFILL) wait_vmcnt<LPS * (STAGES - 2)>();
+          else wait_vmcnt<0>();
           barrier();
         }
         const int rs = (i + 1) % STAGES, ws = i % STAGES;
@@ -455,16 +482,34 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         });
         wait_lgkmcnt0();
       };
-      auto step = [&](int i, auto cur_c) {
-        using T = std::true_type;
-        using F = std::false_type;
-        if (i + STAGES < nk) step_body(i, cur_c, T{}, T{});
-        else if (i + 1 < nk) step_body(i, cur_c, T{}, F{});
-        else step_body(i, cur_c, F{}, F{});
+      using T = std::true_type;
+      using F = std::false_type;
+      // the steps after the last refill, starting from buffer parity P
+      auto finish = [&](int i, auto par_c) {
+        constexpr int P = decltype(par_c)::value;
+        using C0 = std::integral_constant<int, P>;
+        using C1 = std::integral_constant<int, P ^ 1>;
+        for (; i + 2 < nk; i += 2) {
+          step_body(i, C0{}, T{}, F{});
+          step_body(i + 1, C1{}, T{}, F{});
+        }
+        if (i + 1 < nk) {
+          step_body(i, C0{}, T{}, F{});
+          step_body(i + 1, C1{}, F{}, F{});
+        } else {
+          step_body(i, C0{}, F{}, F{});
+        }
       };
-      for (int i = 0; i < nk; i += 2) {
-        step(i, std::integral_constant<int, 0>{});
-        if (i + 1 < nk) step(i + 1, std::integral_constant<int, 1>{});
+      int i = 0;
+      for (; i + 1 + STAGES < nk; i += 2) {
+        step_body(i, std::integral_constant<int, 0>{}, T{}, T{});
+        step_body(i + 1, std::integral_constant<int, 1>{}, T{}, T{});
+      }
+      if (i + STAGES < nk) {  // one refilling step is left
+        step_body(i, std::integral_constant<int, 0>{}, T{}, T{});
+        finish(i + 1, std::integral_constant<int, 1>{});
+      } else {
+        finish(i, std::integral_constant<int, 0>{});
       }
     } else {
       // One register buffer: the stage is read right before its compute (the
@@ -477,7 +522,10 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         if (s < nk) issue(s, s);
       auto step_body = [&](int i, auto refill_c) {
         constexpr bool REFILL = decltype(refill_c)::value;
-        wait_stages<LPS, STAGES - 2>(nk - 1 - i);
+        // stage i is complete once min(STAGES-2, nk-1-i) later stages are pending: with
+        // REFILL that is STAGES-2; without, wait for all (one basic block, as above)
+        if constexpr (REFILL) wait_vmcnt<LPS * (STAGES - 2)>();
+        else wait_vmcnt<0>();
         barrier();
         read_stage(i % STAGES, std::integral_constant<int, 0>{});
         const int ws = (i + STAGES - 1) % STAGES;
@@ -486,10 +534,10 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         });
         wait_lgkmcnt0();
       };
-      for (int i = 0; i < nk; ++i) {
-        if (i + STAGES - 1 < nk) step_body(i, std::true_type{});
-        else step_body(i, std::false_type{});
-      }
+      // one body per loop, as in the double-buffered path
+      int i = 0;
+      for (; i + STAGES - 1 < nk; ++i) step_body(i, std::true_type{});
+      for (; i < nk; ++i) step_body(i, std::false_type{});
     }
 
     // ---- split-K: publish the partial with device-coherent stores; the last of the
