@@ -101,22 +101,24 @@ size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
   return (size_t)tiles * split * bm * bn * sizeof(float) + (size_t)tiles * sizeof(int32_t);
 }
 
-// Cost model of the planner (microseconds, measured on MI355X): time of one
-// 128-wide K block of one work unit per tile variant, the fixed cost of a work unit
-// (pipeline fill and epilogue) and the extra cost of a split-K unit (publishing its
-// partial, plus the last arrival reading the other partials). A call's estimate is
+// Cost model of the planner (microseconds, fitted to timings on MI355X): per tile
+// variant, the fixed cost of a work unit (pipeline fill and epilogue) and the time of
+// one 128-wide K block, plus the extra cost of a split-K unit (publishing its partial,
+// plus the last arrival reading the other partials). A call's estimate is
 // rounds * (unit cost) with rounds = ceil(units / CUs), so the planner trades tile
 // efficiency against filling all CUs (the unaligned-block argument of the pages:
 // deepep.org/zh/deepgemm, 非对齐块大小).
-constexpr double kUnitFixedUs = 5.0;
 constexpr double kSplitUnitUs = 6.0;
 constexpr double kSplitReadUsPerKB = 0.125;
 constexpr int kMaxSplit = 8;
-double kb_cost_us(int bm, int bn) {
-  if (bm == 64 && bn == 64) return 0.45;
-  if (bm == 128 && bn == 128) return 0.67;
-  if (bm * bn == 128 * 64) return 0.60;
-  return 1.60;  // 256x128 / 128x256
+struct UnitCost {
+  double fixed_us, kb_us;
+};
+UnitCost unit_cost(int bm, int bn) {
+  if (bm == 64 && bn == 64) return {5.0, 0.45};
+  if (bm == 128 && bn == 128) return {4.5, 0.53};
+  if (bm * bn == 128 * 64) return {5.0, 0.60};
+  return {7.3, 0.94};  // 256x128 / 128x256, 8 waves
 }
 
 // Choose tile shape and split for a call. `rows` is M (dense), M_total
@@ -147,7 +149,8 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
         const int64_t rounds = ceil_div(tiles * split, cus);
         const double reduce =
             split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
-        const double t = (double)rounds * (kUnitFixedUs + kbps * kb_cost_us(v.bm, v.bn) + reduce);
+        const UnitCost c = unit_cost(v.bm, v.bn);
+        const double t = (double)rounds * (c.fixed_us + kbps * c.kb_us + reduce);
         if (t < best * 0.999) {
           best = t;
           pl.bm = v.bm;

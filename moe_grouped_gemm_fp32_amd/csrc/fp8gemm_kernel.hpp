@@ -432,6 +432,11 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
             fb[buf][k % TN], fa[buf][k / TN], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         side(k);
         if (k >= 2) promote(k - 2);
+        // within the slot the MFMA issues first and the promotion FMAs after it, two
+        // MFMAs behind the result they read (left to itself the scheduler hoists them
+        // above the MFMA, and a single wave then waits on every result)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (NMF >= 2) promote(NMF - 2);

@@ -127,6 +127,9 @@ def test_force_config_validation():
     assert L.fp8_gemm_force_config(ctypes.byref(bad)) == -7
     bad = fg.Config(64, 64, 0, 0, 0)
     assert L.fp8_gemm_force_config(ctypes.byref(bad)) == -7
+    auto = fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168)
     with fg.force_config(64, 128, 2):
         assert fg.query_config(fg.KIND_DENSE, 100, 300, 1024)["block_n"] == 128
-    assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168)["block_m"] == 128
+        assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168)["block_m"] == 64
+    # leaving the context restores automatic selection
+    assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168) == auto
