@@ -118,7 +118,7 @@ UnitCost unit_cost(int bm, int bn) {
   if (bm == 64 && bn == 64) return {5.0, 0.45};
   if (bm == 128 && bn == 128) return {4.5, 0.53};
   if (bm * bn == 128 * 64) return {5.0, 0.60};
-  return {7.3, 0.94};  // 256x128 / 128x256, 8 waves
+  return {8.0, 0.88};  // 256x128 / 128x256, 8 waves
 }
 
 // Choose tile shape and split for a call. `rows` is M (dense), M_total

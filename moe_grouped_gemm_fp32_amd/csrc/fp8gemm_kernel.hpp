@@ -94,13 +94,19 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int gm, 
   tn = r / gs;
 }
 
-// LDS layout of a 128-byte operand row: 16-byte chunk c of row `row` is stored at
-// chunk position c ^ swz_key(row). gfx950's LDS has 64 four-byte banks (256 bytes),
-// i.e. two rows share one bank row; a fragment read has 16 lanes fetch the same
-// logical chunk of 16 consecutive rows, and the key (row >> 1) & 7 gives those 16
-// reads 16 distinct 16-byte bank groups (no conflicts).
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz(int row, int c) { return row * kBlockK + ((c ^ swz_key(row)) << 4); }
+// LDS layout of the 128-byte operand rows of a stage. A fragment read (ds_read_b128)
+// has 16 lanes fetch the same logical 16-byte chunk of 16 consecutive rows. Measured
+// on gfx950 with the bank-conflict counter: such a read is conflict-free when each
+// 8-lane half of the 16 lanes stays within one half of the 256-byte bank row
+// (address bit 7), the two halves take opposite halves, and the lanes of a half use
+// distinct 16-byte positions. So within every block of 16 rows, rows 0-7 are stored
+// at the even row positions and rows 8-15 at the odd ones (lds_row), and chunk c of
+// row r sits at chunk position c ^ (r & 7).
+__device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+// the logical row stored at LDS row position R (inverse of lds_row)
+__device__ __forceinline__ int row_at(int R) { return (R & ~15) | ((R >> 1) & 7) | ((R & 1) << 3); }
+__device__ __forceinline__ int swz_key(int row) { return row & 7; }
+__device__ __forceinline__ int swz(int row, int c) { return lds_row(row) * kBlockK + ((c ^ swz_key(row)) << 4); }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima). The s_waitcnt builtin
@@ -306,20 +312,21 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     const uint8_t* Bg = uni(p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK);
     const float* sbg = uni(p.sb + (int64_t)g * p.sb_gstride + kb0);
 
-    // ---- direct-to-LDS load plan. Load instruction r of this wave fills 8 rows
-    // (1 KB) of a stage: lane l writes chunk position l & 7 of row 8*grp + l/8, so it
-    // brings the logical chunk (l & 7) ^ swz_key(row) (the layout above).
+    // ---- direct-to-LDS load plan. Load instruction r of this wave fills LDS row
+    // positions 8*grp .. 8*grp+7 (1 KB) of a stage: lane l writes chunk position l & 7
+    // of position 8*grp + l/8, so it brings the row stored there (row_at) and that
+    // row's logical chunk (l & 7) ^ swz_key(row) (the layout above).
     const int lrow = lane >> 3;
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int r = 0; r < A_INSTR; ++r) {
-      const int row = (r * NW + wave) * 8 + lrow;
+      const int row = row_at((r * NW + wave) * 8 + lrow);
       const int grow = min(m0 + row, p.M - 1);  // rows past the end: clamped, results unused
       a_off[r] = (uint32_t)(grow * p.lda) + (((lane & 7) ^ swz_key(row)) << 4);
     }
 #pragma unroll
     for (int r = 0; r < B_INSTR; ++r) {
-      const int row = (r * NW + wave) * 8 + lrow;
+      const int row = row_at((r * NW + wave) * 8 + lrow);
       const int grow = min(n0 + row, p.N - 1);
       b_off[r] = (uint32_t)(grow * p.ldb) + (((lane & 7) ^ swz_key(row)) << 4);
     }
