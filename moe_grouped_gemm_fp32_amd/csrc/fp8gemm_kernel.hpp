@@ -527,76 +527,72 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       // One register buffer per wave, 8 waves: ping-pong. Waves w and w + 4 share a
       // SIMD; group A (waves 0-3) and group B (waves 4-7) run half a step apart,
       // with a workgroup barrier between phases, so that in every phase one wave of
-      // each SIMD computes a stage from registers (MFMAs, promotions, and its share
-      // of the loads of a later stage) while the other reads its next stage from
-      // LDS. Group B passes one extra barrier before its K loop and group A one after
-      // it, so both pass 2 nk + 1 barriers per unit. Phases, with BAR(n) the n-th
-      // barrier of the unit:
-      //   A: wait(j) BAR(2j+1) read(j) BAR(2j+2) compute(j), loading stage j+S-1
-      //   B: BAR(2j+2) read(j) wait(j+1) BAR(2j+3) compute(j), loading stage j+S
-      // (S = STAGES). Stage j is read by A between BAR(2j+1) and BAR(2j+2) and by B
-      // between BAR(2j+2) and BAR(2j+3); every wave has waited for its own loads of
-      // stage j before BAR(2j+1), and its slot j % S is refilled only after
-      // BAR(2j+3). B's prologue loads S stages, A's S - 1, so each wave's wait(j)
-      // leaves exactly its S - 2 later stages in flight in the steady state.
+      // each SIMD computes a stage from registers (MFMAs and promotions only) while
+      // the other reads its next stage from LDS and issues its share of the loads
+      // of a later stage (a single computing wave is limited by its own instruction
+      // issue, so everything else goes to the reading wave). Group B passes one
+      // extra barrier before its K loop and group A one after it, so both pass
+      // 2 nk + 1 barriers per unit. Phases, with BAR(n) the n-th barrier of the unit
+      // and S = STAGES:
+      //   A: wait(j) BAR(2j+1) read(j)+load(j+S-1) BAR(2j+2) compute(j)
+      //   B: BAR(2j+2) read(j)+load(j+S-1) wait(j+1) BAR(2j+3) compute(j)
+      // Stage j is read by A between BAR(2j+1) and BAR(2j+2) and by B between
+      // BAR(2j+2) and BAR(2j+3); every wave has waited for its own loads of stage j
+      // before BAR(2j+1). Stage j+S-1 goes to the slot of stage j-1, which both
+      // groups finished reading by BAR(2j+1). Both prologues load stages
+      // 0 .. S-2, so each wave's wait leaves exactly its S - 2 later stages in
+      // flight in the steady state.
       static_assert(NW == 8, "single-buffered tiles use 8 waves");
       const bool group_b = wave >= NW / 2;
       using C0 = std::integral_constant<int, 0>;
-      // compute stage j from registers, loading stage `ld` of this wave into its slot
-      auto phase_compute = [&](int ld, auto refill_c) {
+      // read stage j into registers and, with REFILL, load stage `ld` of this wave
+      auto phase_read = [&](int j, int ld, auto refill_c) {
         constexpr bool REFILL = decltype(refill_c)::value;
-        const int slot = ld % STAGES;
-        compute(C0{}, [&](int k) {
-          if constexpr (REFILL) share(k, LPS, [&](int q) { issue_item(ld, slot, q); });
-        });
-      };
-      auto phase_read = [&](int j) {
         read_stage(j % STAGES, C0{});
+        if constexpr (REFILL) issue(ld, ld % STAGES);
         wait_lgkmcnt0();
       };
-      if (!group_b) {
+      auto phase_compute = [&]() { compute(C0{}, [](int) {}); };
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-          if (s < nk) issue(s, s);
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+      if (!group_b) {
         // stage j is complete once min(STAGES-2, nk-1-j) later stages of this wave are
         // pending: STAGES-2 while refills continue, else wait for all (one basic block
-        // per step, as in the double-buffered path)
+        // per phase, as in the double-buffered path)
         int j = 0;
         for (; j + STAGES - 1 < nk; ++j) {
           wait_vmcnt<LPS * (STAGES - 2)>();
           barrier();
-          phase_read(j);
+          phase_read(j, j + STAGES - 1, std::true_type{});
           barrier();
-          phase_compute(j + STAGES - 1, std::true_type{});
+          phase_compute();
         }
         for (; j < nk; ++j) {
           wait_vmcnt<0>();
           barrier();
-          phase_read(j);
+          phase_read(j, 0, std::false_type{});
           barrier();
-          phase_compute(0, std::false_type{});
+          phase_compute();
         }
         barrier();
       } else {
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s)
-          if (s < nk) issue(s, s);
-        wait_stages<LPS, STAGES - 1>(nk - 1);  // stage 0
+        wait_stages<LPS, STAGES - 2>(nk - 1);  // stage 0
         barrier();
         int j = 0;
-        for (; j + STAGES < nk; ++j) {
+        for (; j + STAGES - 1 < nk; ++j) {
           barrier();
-          phase_read(j);
+          phase_read(j, j + STAGES - 1, std::true_type{});
           wait_vmcnt<LPS * (STAGES - 2)>();  // stage j + 1
           barrier();
-          phase_compute(j + STAGES, std::true_type{});
+          phase_compute();
         }
         for (; j < nk; ++j) {
           barrier();
-          phase_read(j);
+          phase_read(j, 0, std::false_type{});
           wait_vmcnt<0>();
           barrier();
-          phase_compute(0, std::false_type{});
+          phase_compute();
         }
       }
     }
