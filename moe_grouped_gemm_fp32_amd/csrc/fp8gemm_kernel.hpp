@@ -166,11 +166,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
-}
-// per-lane 64-bit address (lanes reading from different arrays)
+// 4-byte loads with a per-lane 64-bit address (the scale loads, whose lanes read
+// scattered rows)
 __device__ __forceinline__ void dma4v(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(uni((int)lds)) : "memory");
@@ -204,17 +201,19 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
   constexpr int B_BYTES = BN * kBlockK;
-  constexpr int SA_PER_WAVE = BM / NW;              // activation scales loaded by each wave
-  static_assert(SA_PER_WAVE >= 1 && SA_PER_WAVE <= 64, "scale slots");
-  // scale loads per wave per stage: one when the weight scale fits in lane 63 of the
-  // activation-scale load, else a second one for it
-  constexpr int SC_INSTR = SA_PER_WAVE < 64 ? 1 : 2;
-  constexpr int SC_FLOATS = NW * 64 * SC_INSTR;     // per stage: 64 scale slots per wave per load
+  // Scales of a stage: the BM activation scales, ordered so that the TM scales a lane
+  // needs (rows wm*WTM + 16t + frow, t < TM) are adjacent (one vector read), then 64
+  // slots for the weight scales of the tile's 128-column blocks. Waves below SA_WAVES
+  // each load 64 activation scales, the others the weight scales (identical copies),
+  // so every wave issues one scale load per stage.
+  constexpr int SA_WAVES = BM / 64;
+  static_assert(BM % 64 == 0 && SA_WAVES < NW, "scale loads");
+  static_assert(TM == 1 || TM == 2 || TM == 4, "activation scales per lane: one vector read");
+  constexpr int SC_FLOATS = BM + 64;
   constexpr int STAGE = A_BYTES + B_BYTES + SC_FLOATS * 4;
   constexpr int A_INSTR = A_BYTES / (1024 * NW);    // 1 KB direct-to-LDS loads per wave per stage
   constexpr int B_INSTR = B_BYTES / (1024 * NW);
-  constexpr int LPS = A_INSTR + B_INSTR + SC_INSTR;
-  constexpr int SB_SLOT = SC_INSTR == 1 ? 63 : 64;  // weight scale of a wave within its scale slots
+  constexpr int LPS = A_INSTR + B_INSTR + 1;
   static_assert(LPS * (STAGES - 1) < 64, "vmcnt capacity");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE];
@@ -330,18 +329,24 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       const int grow = min(n0 + row, p.N - 1);
       b_off[r] = (uint32_t)(grow * p.ldb) + (((lane & 7) ^ swz_key(row)) << 4);
     }
-    // scale loads: lanes [0, BM/NW) bring activation scales of rows wave*BM/NW + lane
-    // and this wave's weight scale goes to slot SB_SLOT (lane 63 of the same load, or
-    // every lane of a second load); spare lanes repeat lane 0's address
-    const float* sb_src = uni(sbg + (int64_t)(min(n0 + wn * WTN, p.N - 1) / kBlockK) * p.num_kb);
+    // scale load of this wave (layout above): lane l of activation-scale wave w fills
+    // slot 64w + l, which holds row wm*WTM + 16t + frow for slot wm*WTM + frow*TM + t;
+    // lane l of a weight-scale wave brings the scale of the tile's 128-column block l
+    // (spare lanes repeat the last block)
     const float* sc_src;
-    if (SC_INSTR == 1 && lane == 63) {
-      sc_src = sb_src;
-    } else {
-      const int row = wave * SA_PER_WAVE + (lane < SA_PER_WAVE ? lane : 0);
+    int64_t sc_step;  // per K block
+    if (wave < SA_WAVES) {
+      const int slot = wave * 64 + lane;
+      const int rem = slot % WTM;
+      const int row = (slot / WTM) * WTM + 16 * (rem % TM) + rem / TM;
       sc_src = sag + min(m0 + row, p.M - 1);
+      sc_step = p.ld_sa;
+    } else {
+      constexpr int NB = BN >= kBlockK ? BN / kBlockK : 1;
+      const int nb = min(lane, NB - 1);
+      sc_src = sbg + (int64_t)(min(n0 + nb * kBlockK, p.N - 1) / kBlockK) * p.num_kb;
+      sc_step = 1;
     }
-    const int64_t sc_step = (SC_INSTR == 1 && lane == 63) ? 1 : p.ld_sa;  // per K block
 
     const uint32_t ring = lds_addr(smem);
     // load item q (0 <= q < LPS) of K block kb0 + i into `stage`: A rows, B rows, scales
@@ -352,10 +357,8 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       } else if (q < A_INSTR + B_INSTR) {
         const int r = q - A_INSTR;
         dma16(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
-      } else if (q == A_INSTR + B_INSTR) {
-        dma4v(sc_src + i * sc_step, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR);
       } else {
-        dma4(sb_src + i, 0u, base + A_BYTES + B_BYTES + wave * 256 * SC_INSTR + 256);
+        dma4v(sc_src + i * sc_step, base + A_BYTES + B_BYTES + (wave < SA_WAVES ? wave * 256 : BM * 4));
       }
     };
     auto issue = [&](int i, int stage) {
@@ -371,12 +374,6 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
 
     const int frow = lane & 15;          // fragment row within a 16-row subtile
     const int fchunk = (lane >> 4) * 2;  // first of the lane's two 16-byte K chunks
-    int sa_slot[TM];
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const int row = wm * WTM + 16 * t + frow;
-      sa_slot[t] = (row / SA_PER_WAVE) * 64 * SC_INSTR + row % SA_PER_WAVE;
-    }
     // fragments and scales of one stage, read from LDS into registers. Read item q:
     // B fragments first, then the scales, then the A fragments, so a compute that
     // starts before all reads have landed needs only the oldest ones.
@@ -398,9 +395,19 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
         fb[buf][q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else if (q == TN) {
-        sb_r[buf] = sS[wave * 64 * SC_INSTR + SB_SLOT];
+        sb_r[buf] = sS[BM + (wn * WTN) / kBlockK];
+        const float* sa_p = sS + wm * WTM + frow * TM;
+        if constexpr (TM == 4) {
+          const v4f v = *reinterpret_cast<const v4f*>(sa_p);
 #pragma unroll
-        for (int t = 0; t < TM; ++t) sa_r[buf][t] = sS[sa_slot[t]];
+          for (int t = 0; t < TM; ++t) sa_r[buf][t] = v[t];
+        } else if constexpr (TM == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(sa_p);
+          sa_r[buf][0] = v.x;
+          sa_r[buf][1] = v.y;
+        } else {
+          sa_r[buf][0] = sa_p[0];
+        }
       } else {
         const int t = q - TN - 1;
         const int row = wm * WTM + 16 * t + frow;
