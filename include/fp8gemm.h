@@ -28,9 +28,9 @@
  *  - e4m3 = OCP E4M3FN bytes (max 448; 0x7F/0xFF are NaN). bf16 = uint16 bits.
  *  - Strides are in ELEMENTS of the pointed-to type. K % 128 == 0.
  *    lda, ldb >= K and multiples of 16; ldd >= N; ld_sa >= the number of rows it
- *    covers and a multiple of 4; A, B 16-byte aligned, D 2-byte aligned (8-byte
- *    aligned with ldd % 4 == 0 for the fast 8-byte store path), sa / sb 4-byte
- *    aligned.
+ *    covers and a multiple of 4; A, B 16-byte aligned, D 2-byte aligned (the
+ *    fastest, 16-byte stores need D 16-byte aligned and ldd % 8 == 0; 8-byte
+ *    stores D 8-byte aligned and ldd % 4 == 0), sa / sb 4-byte aligned.
  *  - Rounding: FP32 accumulation, one round-to-nearest-even to BF16 per output.
  *  - Return value: FP8GEMM_OK (0) or a negative FP8GEMM_ERR_* code. On an
  *    argument error nothing is launched. No exception crosses the ABI.

@@ -247,7 +247,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.num_kb = K / fp8gemm::kBlockK;
   p.num_units = (int)pl.units;
   p.group_m = 8;
-  p.vec_store = (p.ldd % 4 == 0) && aligned(p.D, 8);
+  p.vec_store = (p.ldd % 8 == 0 && aligned(p.D, 16)) ? 2 : (p.ldd % 4 == 0 && aligned(p.D, 8)) ? 1 : 0;
   if (pl.split > 1) {
     const int64_t tiles = pl.units / pl.split;
     p.ws = static_cast<float*>(workspace);

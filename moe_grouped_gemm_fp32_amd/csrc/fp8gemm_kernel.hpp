@@ -19,10 +19,12 @@
 // unit.
 //
 // MFMA operand roles: the MFMA's first operand carries 16 rows of B (n) and the
-// second 16 rows of A (m), so lane l of the 16x16 result holds
-// D[m0 + l%16][n0 + 4*(l/16) + r], r = 0..3: four consecutive columns of one row
-// (one 8-byte BF16 store) and a single activation scale per lane. Both operands
-// use the same lane->K assignment, so the K order inside the MFMA is irrelevant.
+// second 16 rows of A (m), so lane l of a 16x16 result holds four B rows 4*(l/16)+r
+// of one A row l%16: a single activation scale per lane. B rows are placed so that
+// the lane's results of subtiles 2h and 2h+1 are eight consecutive output columns
+// (b_col): one 16-byte BF16 store per lane, 64 contiguous bytes per row. Both
+// operands use the same lane->K assignment, so the K order inside the MFMA is
+// irrelevant.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,7 +57,8 @@ struct Params {
   int split_k, kb_per_split, num_kb;
   int num_units;             // dense / contiguous: tiles * split_k (masked: computed on device)
   int group_m;               // raster group height in tiles
-  int vec_store;             // D rows allow 8-byte stores (ldd % 4 == 0, D 8-byte aligned)
+  int vec_store;             // widest D store: 2 = 16 bytes (ldd % 8 == 0, D 16-byte aligned),
+                             // 1 = 8 bytes (ldd % 4 == 0, D 8-byte aligned), 0 = 2 bytes
   float* ws;                 // split-K partials [tile][split][BM*BN]
   int32_t* counters;         // split-K arrival counters [tile]
 };
@@ -64,12 +67,30 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// FP32 -> BF16 bits, round to nearest, ties to even; NaN -> canonical quiet NaN.
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two FP32 values to packed BF16 bits (a in the low half), rounded to nearest even by
+// one v_cvt_pk_bf16_f32. The kernel's float mode keeps FP32 denormals, so subnormal
+// results round like normal ones; values past the BF16 range become infinities. (NaN
+// inputs are outside the interface contract.)
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+}
+
+// Eight BF16 values (packed in w, lowest column first) to dst[0..7], of which only the
+// first `left` columns exist; `vec` is the widest store the row alignment allows.
+__device__ __forceinline__ void store_edge(uint16_t* dst, uint4 w, int left, int vec) {
+  if (left >= 8 && vec == 2) {
+    *reinterpret_cast<uint4*>(dst) = w;
+  } else if (left >= 8 && vec == 1) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
+    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(w.z, w.w);
+  } else {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < left) dst[c] = (uint16_t)(d[c >> 1] >> (16 * (c & 1)));
+  }
 }
 
 // Bijection on [0, U) that gives each XCD one contiguous range of logical units:
@@ -103,6 +124,12 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int gm, 
 // at the even row positions and rows 8-15 at the odd ones (lds_row), and chunk c of
 // row r sits at chunk position c ^ (r & 7).
 __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+// output column (within the tile) of logical B row x: inside each 32-row group,
+// row 16j' + 4q + r (j' = 0, 1) holds column 8q + 4j' + r, so a lane's four rows of
+// subtile 2h and of 2h+1 are the eight columns 32h + 8q .. 32h + 8q + 7
+__device__ __forceinline__ int b_col(int x) {
+  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
 // the logical row stored at LDS row position R (inverse of lds_row)
 __device__ __forceinline__ int row_at(int R) { return (R & ~15) | ((R >> 1) & 7) | ((R & 1) << 3); }
 __device__ __forceinline__ int swz_key(int row) { return row & 7; }
@@ -197,6 +224,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   constexpr int TN = WTN / 16;
   static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   static_assert(kBlockK % WTN == 0, "a wave's columns must share one 128-column scale block");
+  static_assert(TN % 2 == 0, "subtiles pair up into 16-byte stores");
   static_assert((BM * kBlockK) % (1024 * NW) == 0 && (BN * kBlockK) % (1024 * NW) == 0, "tile load split");
   static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
@@ -326,7 +354,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
 #pragma unroll
     for (int r = 0; r < B_INSTR; ++r) {
       const int row = row_at((r * NW + wave) * 8 + lrow);
-      const int grow = min(n0 + row, p.N - 1);
+      const int grow = min(n0 + b_col(row), p.N - 1);
       b_off[r] = (uint32_t)(grow * p.ldb) + (((lane & 7) ^ swz_key(row)) << 4);
     }
     // scale load of this wave (layout above): lane l of activation-scale wave w fills
@@ -650,30 +678,29 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       if (tid == 0) __hip_atomic_store(&p.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- epilogue: BF16 round-to-nearest-even, live rows only
+    // ---- epilogue: BF16 round-to-nearest-even, live rows only; subtiles 2h and 2h+1
+    // of a lane are eight consecutive columns (b_col)
     uint16_t* Dg = p.D + (MASKED ? (int64_t)g * p.d_gstride : 0);
     int live_rows = p.M;
     if (MASKED) live_rows = min(max(p.masked_m[g], 0), p.M);
+    const bool full = p.vec_store == 2 && n0 + BN <= p.N;  // no column edge in this tile
+    const int ncol = n0 + wn * WTN + 8 * (lane >> 4);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int m = m0 + wm * WTM + 16 * t + (lane & 15);
       bool ok = m < live_rows;
       if (ok && p.kind == kContiguous) ok = p.m_indices[m] >= 0;
       if (!ok) continue;
-      uint16_t* drow = Dg + (int64_t)m * p.ldd;
+      uint16_t* drow = Dg + (int64_t)m * p.ldd + ncol;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WTN + 16 * j + 4 * (lane >> 4);
-        const v4f v = acc[t][j];
-        if (p.vec_store && n + 3 < p.N) {
-          const uint32_t lo = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-          const uint32_t hi = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-          *reinterpret_cast<uint2*>(drow + n) = make_uint2(lo, hi);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < p.N) drow[n + r] = (uint16_t)bf16_bits(v[r]);
-        }
+      for (int h = 0; h < TN / 2; ++h) {
+        const v4f u = acc[t][2 * h], v = acc[t][2 * h + 1];
+        const uint4 w = make_uint4(bf16x2_bits(u[0], u[1]), bf16x2_bits(u[2], u[3]), bf16x2_bits(v[0], v[1]),
+                                   bf16x2_bits(v[2], v[3]));
+        if (full)
+          *reinterpret_cast<uint4*>(drow + 32 * h) = w;
+        else
+          store_edge(drow + 32 * h, w, p.N - (ncol + 32 * h), p.vec_store);
       }
     }
   }

@@ -125,6 +125,32 @@ def test_strided_operands(cuda_device):
     assert np.all(bits_of(Dbig)[:, N:] == SENT), "columns beyond N must not be written"
 
 
+@pytest.mark.parametrize("col0,pitch_mod8", [(0, 4), (4, 0), (1, 0), (2, 3), (0, 0)],
+                         ids=["ldd%8=4", "D+8B", "D+2B", "odd_ldd", "aligned"])
+@pytest.mark.parametrize("N", [192, 252])
+def test_output_alignment_and_pitch(cuda_device, col0, pitch_mod8, N):
+    # D rows of every alignment the store widths distinguish (16-, 8- and 2-byte), with
+    # column edges inside a tile (N=252); cells around the output keep the sentinel
+    M, K = 80, 384
+    c = synth.dense_case(M, N, K, seed=91 + col0 + N, device=cuda_device)
+    ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
+    pitch = (N + col0 + 15) // 8 * 8 + pitch_mod8
+    for tile in (None, (64, 64, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1)):
+        big = synth.sentinel_output((M + 1, pitch), cuda_device)
+        D = big[:M, col0:col0 + N]
+        if tile is None:
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D)
+        else:
+            with fg.force_config(*tile):
+                fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D)
+        torch.cuda.synchronize()
+        out = bits_of(big)
+        compare("normal", out[:M, col0:col0 + N], ref, f"pitch {pitch} col0 {col0} N {N} {tile}")
+        keep = np.ones(out.shape, dtype=bool)
+        keep[:M, col0:col0 + N] = False
+        assert np.all(out[keep] == SENT), f"cells outside D written: {tile}"
+
+
 @pytest.mark.parametrize("M,N,K,tile", [(64, 2112, 7168, None), (128, 4096, 7168, None), (100, 384, 2048, (64, 64, 8)),
                                         (256, 640, 4096, (128, 128, 5))])
 def test_split_k_workspace_reuse_with_new_inputs(cuda_device, M, N, K, tile):
