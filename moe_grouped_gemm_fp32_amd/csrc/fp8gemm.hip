@@ -110,6 +110,12 @@ size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
 // deepep.org/zh/deepgemm, 非对齐块大小).
 constexpr double kSplitUnitUs = 6.0;
 constexpr double kSplitReadUsPerKB = 0.125;
+// A call also takes at least its HBM traffic (A, B and D once, plus the split-K
+// partials, written and read once each) over the read rate measured when the
+// Infinity Cache holds dirty lines of an earlier output, as it does between
+// back-to-back GEMMs: about 1.9 TB/s. For few-row shapes, which stream B once, this
+// bound decides between tiles and splits that the per-unit costs rank wrongly.
+constexpr double kHbmBytesPerUs = 1.9e6;
 constexpr int kMaxSplit = 8;
 struct UnitCost {
   double fixed_us, kb_us;
@@ -131,7 +137,7 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     pl.bn = g_forced_cfg.block_n;
     pl.split = std::max(1, g_forced_cfg.split_k);
   } else {
-    double best = 1e30;
+    double best = 1e30, best_units = 1e30;
     const int live = kind == FP8GEMM_KIND_MASKED ? std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows))
                                                  : rows;
     for (const auto& v : kVariants) {
@@ -150,9 +156,15 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
         const double reduce =
             split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
         const UnitCost c = unit_cost(v.bm, v.bn);
-        const double t = (double)rounds * (c.fixed_us + kbps * c.kb_us + reduce);
-        if (t < best * 0.999) {
+        const double hbm_bytes = (double)rows * K * (kind == FP8GEMM_KIND_MASKED ? G : 1) +
+                                 (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) + 2.0 * rows * N +
+                                 (split > 1 ? 8.0 * split * ceil_div(rows, v.bm) * v.bm * N : 0.0);
+        const double t_units = (double)rounds * (c.fixed_us + kbps * c.kb_us + reduce);
+        const double t = std::max(t_units, hbm_bytes / kHbmBytesPerUs);
+        // ties of the bound (calls that stream the same bytes) go to the faster units
+        if (t < best * 0.999 || (t < best * 1.001 && t_units < best_units)) {
           best = t;
+          best_units = t_units;
           pl.bm = v.bm;
           pl.bn = v.bn;
           pl.split = split;

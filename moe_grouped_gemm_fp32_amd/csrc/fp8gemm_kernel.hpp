@@ -211,6 +211,71 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
+// Split-K: publish this split's partial (acc, each 16x16 result stored lane-major at
+// frag_base + (t * TN + j) * 64 in units of 4 floats) with device-coherent stores and
+// count the arrival; the last of the S arrivals reads the other partials with
+// device-coherent loads and sums all S in split order into acc, then resets the
+// counter. Returns true for the workgroup that writes the tile. Every thread of the
+// workgroup calls it (it contains workgroup barriers).
+template <int TM, int TN>
+__device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN], int tile_id, int split, int S,
+                                              int frag_base, int tile_floats, int tid, int* s_flag) {
+  float* tile_ws = p.ws + (int64_t)tile_id * S * tile_floats;
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      float* dst = tile_ws + (int64_t)split * tile_floats + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, acc[t][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  wait_vmcnt<0>();  // the partial has reached the device-coherent level
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&p.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (old == S - 1);
+  }
+  __syncthreads();
+  const int last = *s_flag;
+  __syncthreads();
+  if (!last) return false;
+  // per partial, all loads are issued before the first use: one round trip per split
+  v4f sum[TM][TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sum[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < S; ++q) {
+    if (q == split) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sum[t][j] += acc[t][j];
+    } else {
+      v4f part[TM][TN];
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float* src = tile_ws + (int64_t)q * tile_floats + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            part[t][j][r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sum[t][j] += part[t][j];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[t][j] = sum[t][j];
+  if (tid == 0) __hip_atomic_store(&p.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // BM x BN tile, WAVES_M x WAVES_N wave64s (4 or 8), STAGES-deep LDS ring; MASKED
 // instances carry the per-group live-tile table.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED>
@@ -632,51 +697,9 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       }
     }
 
-    // ---- split-K: publish the partial with device-coherent stores; the last of the
-    // S arrivals reads the others (device-coherent loads) and reduces in split order
-    if (S > 1) {
-      float* tile_ws = p.ws + (int64_t)tile_id * S * (BM * BN);
-      const int frag_base = (wave * TM * TN) * 64 + lane;
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          float* dst = tile_ws + (int64_t)split * (BM * BN) + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            __hip_atomic_store(dst + r, acc[t][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      wait_vmcnt<0>();  // the partial has reached the device-coherent level
-      __syncthreads();
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(&p.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_info = (old == S - 1);
-      }
-      __syncthreads();
-      const int last = s_info;
-      __syncthreads();
-      if (!last) continue;
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-          for (int q = 0; q < S; ++q) {
-            v4f part;
-            if (q == split) {
-              part = acc[t][j];
-            } else {
-              const float* src = tile_ws + (int64_t)q * (BM * BN) + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                part[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            sum += part;
-          }
-          acc[t][j] = sum;
-        }
-      if (tid == 0) __hip_atomic_store(&p.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // ---- split-K: the last of the S arrivals writes the tile
+    if (S > 1 && !reduce_splits(p, acc, tile_id, split, S, (wave * TM * TN) * 64 + lane, BM * BN, tid, &s_info))
+      continue;
 
     // ---- epilogue: BF16 round-to-nearest-even, live rows only; subtiles 2h and 2h+1
     // of a lane are eight consecutive columns (b_col)
