@@ -71,7 +71,10 @@ typedef struct {
   int block_n;    /* output columns per work unit                                */
   int split_k;    /* K splits per output tile (1 = none; > 1 uses the workspace) */
   int grid;       /* workgroups launched (persistent loop over work units)       */
-  int num_units;  /* work units (tiles x splits); an upper bound for masked      */
+  int num_units;  /* work units; an upper bound for masked                       */
+  int full_tiles; /* tiles computed whole, the first in the order of work; each  */
+                  /* other tile is split_k units. A last, partial round of tiles */
+                  /* is split this way so that it occupies every CU.            */
 } fp8gemm_config_t;
 
 /*
@@ -140,7 +143,8 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m,
                           size_t workspace_bytes, fp8gemm_config_t* out);
 
 /* Force the tile configuration of later calls (tuning and tests): block_m,
- * block_n and split_k are used, grid and num_units are ignored. NULL restores
+ * block_n, split_k and full_tiles (clamped to the tile count; 0 splits every
+ * tile) are used, grid and num_units are ignored. NULL restores
  * automatic selection. Not thread-safe; process-wide.
  * Returns FP8GEMM_ERR_CONFIG for a tile shape that has no kernel. */
 int fp8_gemm_force_config(const fp8gemm_config_t* cfg);

@@ -41,7 +41,7 @@ class Fp8GemmError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("split_k", ctypes.c_int),
-                ("grid", ctypes.c_int), ("num_units", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("num_units", ctypes.c_int), ("full_tiles", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -223,9 +223,10 @@ def query_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int 
 
 
 @contextlib.contextmanager
-def force_config(block_m: int, block_n: int, split_k: int = 1):
-    """Context manager forcing a tile configuration (tests and tuning)."""
-    cfg = Config(block_m, block_n, split_k, 0, 0)
+def force_config(block_m: int, block_n: int, split_k: int = 1, full_tiles: int = 0):
+    """Context manager forcing a tile configuration (tests and tuning); the first
+    `full_tiles` tiles are computed whole, the others split `split_k` ways."""
+    cfg = Config(block_m, block_n, split_k, 0, 0, full_tiles)
     _check(lib().fp8_gemm_force_config(ctypes.byref(cfg)), "fp8_gemm_force_config")
     try:
         yield

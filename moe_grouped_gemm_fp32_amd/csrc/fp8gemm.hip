@@ -74,6 +74,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
   int bm = 128, bn = 128, split = 1, kbps = 1, tiles_m = 0, tiles_n = 0;
+  int64_t full = 0;  // leading tiles computed whole (the others are split `split` ways)
   int64_t units = 0;
   int grid = 0;
   size_t ws_bytes = 0;
@@ -136,39 +137,52 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     pl.bm = g_forced_cfg.block_m;
     pl.bn = g_forced_cfg.block_n;
     pl.split = std::max(1, g_forced_cfg.split_k);
+    pl.full = std::max(0, g_forced_cfg.full_tiles);
   } else {
     double best = 1e30, best_units = 1e30;
     const int live = kind == FP8GEMM_KIND_MASKED ? std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows))
                                                  : rows;
+    // candidate: `full` tiles computed whole, the other tiles split `split` ways
+    auto consider = [&](const Variant& v, int64_t tiles, int split, int64_t full) {
+      const int kbps = (int)ceil_div(num_kb, split);
+      const int64_t split_tiles = split > 1 ? tiles - full : 0;
+      if (split > 1 && split_ws_bytes(split_tiles, split, v.bm, v.bn) > ws_avail) return;
+      const UnitCost c = unit_cost(v.bm, v.bn);
+      const double reduce =
+          split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
+      double t_units;
+      if (split > 1 && full > 0) {  // whole tiles fill full / cus rounds, the split tiles one more
+        t_units = (double)(full / cus) * (c.fixed_us + num_kb * c.kb_us) + (c.fixed_us + kbps * c.kb_us + reduce);
+      } else {
+        const int64_t units = split > 1 ? tiles * split : tiles;
+        t_units = (double)ceil_div(units, cus) * (c.fixed_us + (split > 1 ? kbps : num_kb) * c.kb_us + reduce);
+      }
+      const double hbm_bytes = (double)rows * K * (kind == FP8GEMM_KIND_MASKED ? G : 1) +
+                               (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) + 2.0 * rows * N +
+                               8.0 * split * split_tiles * v.bm * v.bn;
+      const double t = std::max(t_units, hbm_bytes / kHbmBytesPerUs);
+      // ties of the bound (calls that stream the same bytes) go to the faster units
+      if (t < best * 0.999 || (t < best * 1.001 && t_units < best_units)) {
+        best = t;
+        best_units = t_units;
+        pl.bm = v.bm;
+        pl.bn = v.bn;
+        pl.split = split;
+        pl.full = split > 1 ? full : tiles;
+      }
+    };
     for (const auto& v : kVariants) {
       if (kind == FP8GEMM_KIND_CONTIGUOUS && 128 % v.bm != 0) continue;  // one expert per tile
       if (v.bm >= 2 * 128 && live <= 128) continue;                      // mostly empty tiles
       const int64_t tiles =
           ceil_div(live, v.bm) * ceil_div(N, v.bn) * (kind == FP8GEMM_KIND_MASKED ? G : 1);
       const int max_split = kind == FP8GEMM_KIND_MASKED ? 1 : std::min(num_kb, kMaxSplit);
+      const int64_t rem = tiles % cus;  // tiles of a last, partial round
       for (int sp = 1; sp <= max_split; ++sp) {
-        const int kbps = (int)ceil_div(num_kb, sp);
-        const int split = (int)ceil_div(num_kb, kbps);
-        if (split != sp) continue;  // same as a smaller split
-        if (split > 1 && split_ws_bytes(ceil_div(rows, v.bm) * ceil_div(N, v.bn), split, v.bm, v.bn) > ws_avail)
-          continue;
-        const int64_t rounds = ceil_div(tiles * split, cus);
-        const double reduce =
-            split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
-        const UnitCost c = unit_cost(v.bm, v.bn);
-        const double hbm_bytes = (double)rows * K * (kind == FP8GEMM_KIND_MASKED ? G : 1) +
-                                 (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) + 2.0 * rows * N +
-                                 (split > 1 ? 8.0 * split * ceil_div(rows, v.bm) * v.bm * N : 0.0);
-        const double t_units = (double)rounds * (c.fixed_us + kbps * c.kb_us + reduce);
-        const double t = std::max(t_units, hbm_bytes / kHbmBytesPerUs);
-        // ties of the bound (calls that stream the same bytes) go to the faster units
-        if (t < best * 0.999 || (t < best * 1.001 && t_units < best_units)) {
-          best = t;
-          best_units = t_units;
-          pl.bm = v.bm;
-          pl.bn = v.bn;
-          pl.split = split;
-        }
+        if ((int)ceil_div(num_kb, ceil_div(num_kb, sp)) != sp) continue;  // same as a smaller split
+        consider(v, tiles, sp, 0);
+        // whole tiles for the full rounds, the last partial round split over the CUs
+        if (sp > 1 && tiles > cus && rem > 0 && rem * sp <= cus) consider(v, tiles, sp, tiles - rem);
       }
     }
   }
@@ -177,13 +191,15 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   pl.tiles_n = (int)ceil_div(N, pl.bn);
   pl.tiles_m = (int)ceil_div(rows, pl.bm);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (kind == FP8GEMM_KIND_MASKED ? G : 1);
-  pl.ws_bytes = split_ws_bytes(tiles, pl.split, pl.bm, pl.bn);
+  pl.full = pl.split > 1 && kind != FP8GEMM_KIND_MASKED ? std::min<int64_t>(pl.full, tiles) : tiles;
+  pl.ws_bytes = split_ws_bytes(tiles - pl.full, pl.split, pl.bm, pl.bn);
   if (pl.split > 1 && pl.ws_bytes > ws_avail && !g_forced) {
     pl.split = 1;
     pl.kbps = num_kb;
+    pl.full = tiles;
     pl.ws_bytes = 0;
   }
-  pl.units = tiles * pl.split;
+  pl.units = pl.full + (tiles - pl.full) * pl.split;
   const int64_t cap = (int64_t)cus * kOccupancy;
   int64_t grid = std::min<int64_t>(pl.units, cap);
   if (grid > fp8gemm::kNumXcd) grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;  // keep XCD mapping
@@ -258,13 +274,14 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.kb_per_split = pl.kbps;
   p.num_kb = K / fp8gemm::kBlockK;
   p.num_units = (int)pl.units;
+  p.full_tiles = (int)pl.full;
   p.group_m = 8;
   p.vec_store = (p.ldd % 8 == 0 && aligned(p.D, 16)) ? 2 : (p.ldd % 4 == 0 && aligned(p.D, 8)) ? 1 : 0;
   if (pl.split > 1) {
-    const int64_t tiles = pl.units / pl.split;
+    const int64_t split_tiles = (pl.units - pl.full) / pl.split;
     p.ws = static_cast<float*>(workspace);
     p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                            (size_t)tiles * pl.split * pl.bm * pl.bn * sizeof(float));
+                                            (size_t)split_tiles * pl.split * pl.bm * pl.bn * sizeof(float));
   }
   if (pl.units == 0) return FP8GEMM_OK;
   return launch(pl, p, stream) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
@@ -362,6 +379,7 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m, 
   out->split_k = pl.split;
   out->grid = pl.grid;
   out->num_units = (int)pl.units;
+  out->full_tiles = (int)pl.full;
   return FP8GEMM_OK;
 }
 

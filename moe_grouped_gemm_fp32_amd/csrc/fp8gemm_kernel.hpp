@@ -55,12 +55,14 @@ struct Params {
   int kind;
   int tiles_m, tiles_n;      // tiles_m per group for masked
   int split_k, kb_per_split, num_kb;
+  int full_tiles;            // dense / contiguous: leading tiles of the work order computed
+                             // whole; each later tile is split_k units (split-K)
   int num_units;             // dense / contiguous: tiles * split_k (masked: computed on device)
   int group_m;               // raster group height in tiles
   int vec_store;             // widest D store: 2 = 16 bytes (ldd % 8 == 0, D 16-byte aligned),
                              // 1 = 8 bytes (ldd % 4 == 0, D 8-byte aligned), 0 = 2 bytes
-  float* ws;                 // split-K partials [tile][split][BM*BN]
-  int32_t* counters;         // split-K arrival counters [tile]
+  float* ws;                 // split-K partials [split tile][split][BM*BN]
+  int32_t* counters;         // split-K arrival counters [split tile]
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -212,34 +214,38 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 
 // Split-K: publish this split's partial (acc, each 16x16 result stored lane-major at
-// frag_base + (t * TN + j) * 64 in units of 4 floats) with device-coherent stores and
-// count the arrival; the last of the S arrivals reads the other partials with
-// device-coherent loads and sums all S in split order into acc, then resets the
-// counter. Returns true for the workgroup that writes the tile. Every thread of the
-// workgroup calls it (it contains workgroup barriers).
+// frag_base + (t * TN + j) * 64 in units of 4 floats) and count the arrival; the last
+// of the S arrivals reads the other partials and sums all S in split order into acc,
+// then resets the counter. Returns true for the workgroup that writes the tile.
+// Every thread of the workgroup calls it (it contains workgroup barriers).
+// Partials move as device-coherent (sc1) 16-byte buffer accesses, one kilobyte of
+// contiguous lines per instruction; the last arrival issues all loads of a partial
+// before adding any of them, so each partial costs one round trip.
 template <int TM, int TN>
-__device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN], int tile_id, int split, int S,
+__device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN], int ws_id, int split, int S,
                                               int frag_base, int tile_floats, int tid, int* s_flag) {
-  float* tile_ws = p.ws + (int64_t)tile_id * S * tile_floats;
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  constexpr int kDeviceScope = 16;       // buffer cache policy: sc1
+  constexpr int kRawDword3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, untyped access
+  float* tile_ws = const_cast<float*>(uni((const float*)(p.ws + (int64_t)ws_id * S * tile_floats)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tile_ws, 0, S * tile_floats * 4, kRawDword3);
+  auto offset = [&](int q, int t, int j) { return (q * tile_floats + (frag_base + (t * TN + j) * 64) * 4) * 4; };
 #pragma unroll
   for (int t = 0; t < TM; ++t)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      float* dst = tile_ws + (int64_t)split * tile_floats + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, acc[t][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int j = 0; j < TN; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[t][j]), rs, offset(split, t, j), 0,
+                                             kDeviceScope);
   wait_vmcnt<0>();  // the partial has reached the device-coherent level
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&p.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(&p.counters[ws_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = (old == S - 1);
   }
   __syncthreads();
   const int last = *s_flag;
   __syncthreads();
   if (!last) return false;
-  // per partial, all loads are issued before the first use: one round trip per split
   v4f sum[TM][TN];
 #pragma unroll
   for (int t = 0; t < TM; ++t)
@@ -256,12 +262,8 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
 #pragma unroll
       for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float* src = tile_ws + (int64_t)q * tile_floats + (int64_t)(frag_base + (t * TN + j) * 64) * 4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            part[t][j][r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int j = 0; j < TN; ++j)
+          part[t][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, offset(q, t, j), 0, kDeviceScope));
 #pragma unroll
       for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -272,7 +274,7 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
   for (int t = 0; t < TM; ++t)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[t][j] = sum[t][j];
-  if (tid == 0) __hip_atomic_store(&p.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&p.counters[ws_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -356,8 +358,17 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   }
 
   for (int u = blockIdx.x; u < num_units; u += gridDim.x) {
-    const int L = xcd_remap(u, num_units);
-    int g = 0, tm, tn, split, tile_id;
+    // whole tiles and split units are remapped separately, so the split units (a
+    // last, partial round of tiles cut into K slices) stay in the last round
+    int L;
+    if (!MASKED && p.full_tiles > 0 && p.full_tiles < num_units)
+      L = u < p.full_tiles ? xcd_remap(u, p.full_tiles)
+                           : p.full_tiles + xcd_remap(u - p.full_tiles, num_units - p.full_tiles);
+    else
+      L = xcd_remap(u, num_units);
+    int g = 0, tm, tn, split;
+    int S_u = S;       // splits of this unit's tile
+    int ws_id = 0;     // slot of a split tile in the workspace
     if constexpr (MASKED) {
       // units of one (group, n-tile) are contiguous: the group's B tile is reused
       int lo = 0, hi = p.G;  // largest g with s_pre[g] * tiles_n * S <= L
@@ -373,12 +384,25 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       const int r = local - tn * live_tiles * S;
       tm = r / S;
       split = r - tm * S;
-      tile_id = (pre + tm) * p.tiles_n + tn;
     } else {
-      const int tile = L / S;
-      split = L - tile * S;
+      // the first full_tiles tiles are single units; each later one is S units, so a
+      // last partial round of tiles can be spread over all CUs as K slices. Split
+      // units are numbered split-major: the units next to each other (on one XCD)
+      // are neighbouring tiles at the same K slice, which share A and B rows in L2
+      // as the tiles of a whole round do.
+      int tile;
+      if (L < p.full_tiles) {
+        tile = L;
+        split = 0;
+        S_u = 1;
+      } else {
+        const int split_tiles = (num_units - p.full_tiles) / S;
+        const int l = L - p.full_tiles;
+        split = l / split_tiles;
+        ws_id = l - split * split_tiles;
+        tile = p.full_tiles + ws_id;
+      }
       raster(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-      tile_id = tm * p.tiles_n + tn;
     }
     const int m0 = tm * BM;
     const int n0 = tn * BN;
@@ -397,8 +421,8 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       if (g < 0 || g >= p.G) continue;  // all padding (or an invalid id): nothing to write
     }
 
-    const int kb0 = split * p.kb_per_split;
-    const int nk = min(p.num_kb, kb0 + p.kb_per_split) - kb0;
+    const int kb0 = S_u > 1 ? split * p.kb_per_split : 0;
+    const int nk = S_u > 1 ? min(p.num_kb, kb0 + p.kb_per_split) - kb0 : p.num_kb;
     const uint8_t* Ag = uni(p.A + (MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK);
     const float* sag = uni(p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa);
     const uint8_t* Bg = uni(p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK);
@@ -698,7 +722,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     }
 
     // ---- split-K: the last of the S arrivals writes the tile
-    if (S > 1 && !reduce_splits(p, acc, tile_id, split, S, (wave * TM * TN) * 64 + lane, BM * BN, tid, &s_info))
+    if (S_u > 1 && !reduce_splits(p, acc, ws_id, split, S_u, (wave * TM * TN) * 64 + lane, BM * BN, tid, &s_info))
       continue;
 
     // ---- epilogue: BF16 round-to-nearest-even, live rows only; subtiles 2h and 2h+1

@@ -93,7 +93,11 @@ def test_planner_invariants_on_dense_shapes(cus256, M, N, K):
     cfg = fg.query_config(fg.KIND_DENSE, M, N, K)
     bm, bn, s = cfg["block_m"], cfg["block_n"], cfg["split_k"]
     tiles = fg.num_tiles(M, N, bm, bn)
-    assert cfg["num_units"] == tiles * s
+    full = cfg["full_tiles"]
+    assert 0 <= full <= tiles and (s > 1 or full == tiles)
+    assert cfg["num_units"] == full + (tiles - full) * s
+    if s > 1 and full > 0:  # whole tiles for the full rounds, one round of split units
+        assert full % 256 == 0 and (tiles - full) * s <= 256
     nkb = K // 128
     assert 1 <= s <= nkb and (s == 1 or nkb % s == 0 or -(-nkb // s) * (s - 1) < nkb)
     # every split owns at least one K block
@@ -101,12 +105,12 @@ def test_planner_invariants_on_dense_shapes(cus256, M, N, K):
     assert kbps * (s - 1) < nkb
     # the planner does not leave most CUs idle when K allows splitting
     if tiles < 64 and nkb >= 16:
-        assert s > 1 and cfg["num_units"] >= 128
+        assert s > 1 and full == 0 and cfg["num_units"] >= 128
     assert cfg["grid"] <= cfg["num_units"] and cfg["grid"] <= 512
     ws = fg.workspace_size(fg.KIND_DENSE, M, N, K)
     assert (ws > 0) == (s > 1)
     if s > 1:
-        assert ws >= tiles * s * bm * bn * 4 + tiles * 4
+        assert ws >= (tiles - full) * s * bm * bn * 4 + (tiles - full) * 4
         # without a workspace the call falls back to no split
         assert fg.query_config(fg.KIND_DENSE, M, N, K, workspace_bytes=0)["split_k"] == 1
 

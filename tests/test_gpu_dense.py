@@ -151,6 +151,34 @@ def test_output_alignment_and_pitch(cuda_device, col0, pitch_mod8, N):
         assert np.all(out[keep] == SENT), f"cells outside D written: {tile}"
 
 
+@pytest.mark.parametrize("tile,full", [((64, 64, 3), 50), ((128, 128, 2), 5), ((256, 128, 4), 3), ((128, 256, 2), 1),
+                                       ((64, 128, 8), 31), ((128, 64, 5), 0)])
+def test_whole_tiles_then_split_tiles(cuda_device, tile, full):
+    # the first `full` tiles of the work order computed whole, the others as split-K
+    # units: every element equals the unsplit or the all-split result of the same
+    # tile shape, and matches the oracle; two calls share one workspace (the arrival
+    # counters reset themselves)
+    M, N, K = 300, 1000, 1280
+    c = synth.dense_case(M, N, K, seed=5150 + full, device=cuda_device)
+    ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
+    whole, _ = run_dense(c, forced=(tile[0], tile[1], 1))
+    split_all, _ = run_dense(c, forced=tile)
+    tiles = fg.num_tiles(M, N, tile[0], tile[1])
+    ws = torch.zeros(max(16, (tiles - full) * tile[2] * tile[0] * tile[1] * 4 + (tiles - full) * 4),
+                     dtype=torch.uint8, device=cuda_device)
+    for rep in range(2):
+        D = synth.sentinel_output((M, N), cuda_device)
+        with fg.force_config(*tile, full_tiles=full):
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, ws)
+        torch.cuda.synchronize()
+        got = bits_of(D)
+        compare("normal", got, ref, f"{tile} full {full} call {rep}")
+        assert np.all((got == bits_of(whole)) | (got == bits_of(split_all))), f"{tile} full {full}"
+        if 0 < full < tiles:
+            assert np.any(got != bits_of(split_all)) and np.any(got != bits_of(whole)), "both kinds of unit ran"
+    assert int(ws[-(tiles - full) * 4:].view(torch.int32).abs().sum()) == 0 if full < tiles else True
+
+
 @pytest.mark.parametrize("M,N,K,tile", [(64, 2112, 7168, None), (128, 4096, 7168, None), (100, 384, 2048, (64, 64, 8)),
                                         (256, 640, 4096, (128, 128, 5))])
 def test_split_k_workspace_reuse_with_new_inputs(cuda_device, M, N, K, tile):
