@@ -109,23 +109,25 @@ size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
 // rounds * (unit cost) with rounds = ceil(units / CUs), so the planner trades tile
 // efficiency against filling all CUs (the unaligned-block argument of the pages:
 // deepep.org/zh/deepgemm, 非对齐块大小).
-constexpr double kSplitUnitUs = 6.0;
-constexpr double kSplitReadUsPerKB = 0.125;
+constexpr double kSplitUnitUs = 3.0;
+constexpr double kSplitReadUsPerKB = 0.03;
 // A call also takes at least its HBM traffic (A, B and D once, plus the split-K
 // partials, written and read once each) over the read rate measured when the
 // Infinity Cache holds dirty lines of an earlier output, as it does between
-// back-to-back GEMMs: about 1.9 TB/s. For few-row shapes, which stream B once, this
+// back-to-back GEMMs: about 2 TB/s. For few-row shapes, which stream B once, this
 // bound decides between tiles and splits that the per-unit costs rank wrongly.
-constexpr double kHbmBytesPerUs = 1.9e6;
+constexpr double kHbmBytesPerUs = 2.05e6;
 constexpr int kMaxSplit = 8;
 struct UnitCost {
   double fixed_us, kb_us;
 };
 UnitCost unit_cost(int bm, int bn) {
   if (bm == 64 && bn == 64) return {5.0, 0.45};
-  if (bm == 128 && bn == 128) return {4.5, 0.53};
-  if (bm * bn == 128 * 64) return {5.0, 0.60};
-  return {8.0, 0.88};  // 256x128 / 128x256, 8 waves
+  if (bm == 128 && bn == 128) return {9.0, 0.53};
+  if (bm == 128 && bn == 64) return {5.0, 0.60};
+  if (bm == 64 && bn == 128) return {4.0, 0.60};
+  if (bm == 256 && bn == 128) return {8.0, 0.88};
+  return {8.5, 0.88};  // 128x256
 }
 
 // Choose tile shape and split for a call. `rows` is M (dense), M_total
