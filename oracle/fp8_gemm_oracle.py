@@ -188,3 +188,48 @@ def grouped_masked(A, sa, B, sb, masked_m, D_in, rows=None, cols=None):
         S[g, sel] = Sg
         D[g, sel] = bf16_bits_rne(Sg)
     return D, S
+
+
+# ------------------------------------------------------------------ 1x128 quantisation
+# Upstream of every call: activations in FP32 or BF16 -> e4m3 codes plus one FP32
+# scale per row per 128-wide K block, stored K-block-major [K/128, ld_sa] (the layout
+# the GEMM reads). The pages leave the conversion to the user and give no formula
+# (es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout": the
+# library only offers simple PyTorch helpers). Reading used here, all in FP32 with
+# IEEE round-to-nearest-even operations:
+#     s = amax(|x| over the block) / 448      (s = 1 when that is 0)
+#     q = e4m3_rne(x / s)                     (ties to the even code; a quotient past
+#                                              448, reachable only by rounding, is 448)
+_E4M3_POS = E4M3_TABLE[:0x7F]            # codes 0x00..0x7E, increasing values 0..448
+
+
+def e4m3_rne_codes(y: np.ndarray) -> np.ndarray:
+    """float32 values -> nearest e4m3 codes (ties to even code, saturating at 448).
+
+    Positive codes 0x00..0x7E are increasing in value, so the code of the nearest
+    value is its index in that list; the sign bit is copied (-0.0 -> 0x80)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 1, 0x7E)  # _E4M3_POS[hi-1] < a <= ...
+    lo = hi - 1
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= _E4M3_POS[0x7E], 0x7E, code)          # at or past 448
+    code = np.where(a == 0.0, 0, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_1x128(x: np.ndarray):
+    """x [R, K] (float32; BF16 inputs as their float32 values) -> (codes uint8 [R, K],
+    scales float32 [K/128, R])."""
+    x = np.asarray(x, dtype=np.float32)
+    R, K = x.shape
+    assert K % BLOCK == 0
+    xb = x.reshape(R, K // BLOCK, BLOCK)
+    amax = np.max(np.abs(xb), axis=-1)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    y = (xb / s[..., None]).astype(np.float32)
+    return e4m3_rne_codes(y).reshape(R, K), np.ascontiguousarray(s.T)
