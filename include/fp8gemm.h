@@ -133,6 +133,29 @@ int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int6
                                int G, int M_max, int N, int K, int expected_m,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * 1x128 activation quantisation: the step upstream of every call above, producing
+ * the A operand and its scales (one FP32 scale per row per 128-wide K block:
+ * GeekNews topic 19444, intro). The pages leave FP8 conversion to the user
+ * (es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout"); the
+ * reading implemented here, per row and block, in FP32 with IEEE round-to-nearest-
+ * even operations:  s = amax(|x|) / 448 (s = 1 when that is 0),  q = e4m3_rne(x / s)
+ * (correctly rounded division; ties to the even code; at most 448 in magnitude).
+ *   X  [M, K] row-major, row stride ldx (elements), FP32 or BF16 (x_dtype below);
+ *      16-byte aligned, ldx a multiple of 4 (FP32) or 8 (BF16). NaN inputs are
+ *      outside the contract.
+ *   Q  e4m3 [M, K] row-major, row stride ldq; 8-byte aligned, ldq % 8 == 0.
+ *   sa fp32 [K/128][ld_sa]: sa[kb * ld_sa + m], ld_sa >= M and a multiple of 4
+ *      (the GEMMs' activation-scale layout); columns ld_sa > m >= M are untouched.
+ * All pointers are device pointers owned by the caller; the work is enqueued on
+ * `stream`. Errors: FP8GEMM_ERR_NULL, _SHAPE (M < 0, K <= 0 or K % 128), _LAYOUT
+ * (strides, alignment, unknown x_dtype), _DEVICE, _LAUNCH; nothing is launched on an
+ * argument error. M == 0 is a no-op.
+ */
+enum { FP8GEMM_QUANT_BF16 = 0, FP8GEMM_QUANT_FP32 = 1 };
+int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t ldq,
+                       float* sa, int64_t ld_sa, int M, int K, hipStream_t stream);
+
 /* Bytes of split-K workspace the call with these sizes may use (0 = never splits).
  * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked). */
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m);

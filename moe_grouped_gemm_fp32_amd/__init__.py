@@ -27,7 +27,7 @@ __all__ = [
     "fp8_gemm_nt", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
     "workspace_size", "make_workspace", "query_config", "force_config", "set_num_cus",
     "get_num_cus", "get_mk_alignment_for_contiguous_layout", "scale_ld", "num_tiles",
-    "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED",
+    "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED", "quantize_1x128",
     "Fp8GemmError",
 ]
 
@@ -56,6 +56,7 @@ _SIGS = {
     "fp8_grouped_gemm_nt_masked": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
+    "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
     "fp8_gemm_force_config": (_INT, [ctypes.POINTER(Config)]),
     "fp8_gemm_set_num_cus": (_INT, [_INT]),
@@ -153,6 +154,34 @@ def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Te
                            _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt")
     return D
+
+
+QUANT_BF16, QUANT_FP32 = 0, 1  # fp8_quantize_1x128 input types
+
+
+def quantize_1x128(X: torch.Tensor, Q: Optional[torch.Tensor] = None, sa: Optional[torch.Tensor] = None,
+                   stream=None):
+    """1x128 activation quantisation of X [M, K] (bfloat16 or float32, unit inner
+    stride) -> (Q e4m3 bytes [M, K] uint8, sa float32 [K/128, ld_sa]), the A operand
+    layout of the GEMMs: per row and 128-column block s = amax/448 (1 if zero) and
+    q = e4m3_rne(x / s), computed by fp8_quantize_1x128. Q and sa may be given
+    (written in place); by default Q is [M, K] and sa is [K/128, scale_ld(M)]."""
+    _require(X.device.type == "cuda" and X.dim() == 2 and X.stride(-1) == 1, "X must be a 2-D GPU tensor")
+    _require(X.dtype in (torch.bfloat16, torch.float32), "X must be bfloat16 or float32")
+    M, K = X.shape
+    _require(K % 128 == 0, "K must be a multiple of 128")
+    if Q is None:
+        Q = torch.empty(M, K, dtype=torch.uint8, device=X.device)
+    if sa is None:
+        sa = torch.empty(K // 128, scale_ld(M), dtype=torch.float32, device=X.device)
+    Q = _bytes_view(Q)
+    _require(tuple(Q.shape) == (M, K) and Q.stride(-1) == 1 and Q.device == X.device, "Q must be [M, K]")
+    _require(sa.dtype == torch.float32 and sa.shape[0] == K // 128 and sa.stride(-1) == 1 and sa.stride(0) >= M,
+             "sa must be float32 [K/128, >=M]")
+    st = lib().fp8_quantize_1x128(_ptr(X), X.stride(0), QUANT_BF16 if X.dtype == torch.bfloat16 else QUANT_FP32,
+                                  _ptr(Q), Q.stride(0), _ptr(sa), sa.stride(0), M, K, _stream(X.device, stream))
+    _check(st, "fp8_quantize_1x128")
+    return Q, sa
 
 
 def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None):

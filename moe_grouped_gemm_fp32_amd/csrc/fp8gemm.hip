@@ -19,6 +19,7 @@
 #include <mutex>
 
 #include "fp8gemm_kernel.hpp"
+#include "fp8quant_kernel.hpp"
 
 namespace {
 
@@ -358,6 +359,31 @@ int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int6
   (void)workspace;
   (void)workspace_bytes;
   return run(FP8GEMM_KIND_MASKED, "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream);
+}
+
+int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t ldq, float* sa, int64_t ld_sa, int M,
+                       int K, hipStream_t stream) {
+  if (!X || !Q || !sa) return FP8GEMM_ERR_NULL;
+  if (M < 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
+  if (x_dtype != FP8GEMM_QUANT_BF16 && x_dtype != FP8GEMM_QUANT_FP32) return FP8GEMM_ERR_LAYOUT;
+  const int64_t x_align = x_dtype == FP8GEMM_QUANT_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (ldx < K || ldx % x_align != 0 || ldq < K || ldq % 8 != 0 || ld_sa < M || ld_sa % 4 != 0)
+    return FP8GEMM_ERR_LAYOUT;
+  if (!aligned(X, 16) || !aligned(Q, 8) || !aligned(sa, 4)) return FP8GEMM_ERR_LAYOUT;
+  int st;
+  const int cus = effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  const int nkb = K / fp8gemm::kBlockK;
+  const int64_t items = ceil_div(M, 4) * nkb;  // one wave each
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 4), (int64_t)cus * 8));
+  if (x_dtype == FP8GEMM_QUANT_BF16)
+    hipLaunchKernelGGL(fp8gemm::quantize_1x128_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(X), ldx, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb);
+  else
+    hipLaunchKernelGGL(fp8gemm::quantize_1x128_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const float*>(X), ldx, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m) {

@@ -1,0 +1,81 @@
+// Device code of libfp8gemm's 1x128 activation quantisation: FP32 or BF16 rows to
+// e4m3 codes plus one FP32 scale per row per 128-wide K block, written K-block-major
+// [K/128][ld_sa] -- the operand layout of the GEMMs (one scale per row per 128-K
+// block: GeekNews topic 19444, intro; the pages leave the conversion itself to the
+// user, es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout").
+//
+// Per row and block, in FP32 with IEEE round-to-nearest-even operations:
+//     s = amax(|x|) / 448   (s = 1 when that is 0),   q = e4m3_rne(x / s)
+// The division is the correctly rounded one (not a reciprocal multiply), and the
+// conversion is gfx950's v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even); a
+// quotient can exceed 448 only by the rounding of x / s and then still rounds to 448.
+//
+// HBM-bound elementwise work: no LDS, no matrix unit. A wave takes four rows of one
+// 128-column block; the 16 lanes of a row hold 8 consecutive elements each, so every
+// load instruction reads whole lines and every code store writes 128 contiguous bytes
+// per row. The block maximum is reduced across those 16 lanes with shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gemm {
+
+template <typename T>  // uint16_t: BF16 bits; float
+__device__ __forceinline__ void load8(const T* src, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+    x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) quantize_1x128_kernel(const T* X, int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                             float* sa, int64_t ld_sa, int M, int nkb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;  // row within the wave's four
+  const int c = lane & 15;  // 8-element chunk within the block
+  const int64_t items = (int64_t)((M + 3) / 4) * nkb;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < items; it += (int64_t)gridDim.x * 4) {
+    const int rg = (int)(it / nkb);
+    const int kb = (int)(it - (int64_t)rg * nkb);
+    const int r = rg * 4 + g;
+    const bool live = r < M;
+    float x[8];
+    if (live) {
+      load8(X + (int64_t)r * ldx + kb * 128 + c * 8, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    float s = amax / 448.0f;
+    if (!(s > 0.0f)) s = 1.0f;
+    int w0 = 0, w1 = 0;
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, x[1] / s, w0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / s, x[3] / s, w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / s, x[5] / s, w1, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / s, x[7] / s, w1, true);
+    if (live) {
+      *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + kb * 128 + c * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
+      if (c == 0) sa[(int64_t)kb * ld_sa + r] = s;
+    }
+  }
+}
+
+}  // namespace fp8gemm

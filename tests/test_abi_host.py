@@ -137,3 +137,17 @@ def test_force_config_validation():
         assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168)["block_m"] == 64
     # leaving the context restores automatic selection
     assert fg.query_config(fg.KIND_DENSE, 4096, 4096, 7168) == auto
+
+
+def _quant(X=1 << 20, ldx=7168, dt=0, Q=1 << 20, ldq=7168, sa=1 << 20, ld_sa=64, M=64, K=7168):
+    mk = lambda v: P(v) if v else None
+    return fg.lib().fp8_quantize_1x128(mk(X), ldx, dt, mk(Q), ldq, mk(sa), ld_sa, M, K, None)
+
+
+def test_quantize_argument_validation_without_launch():
+    assert _quant(X=0) == -1 and _quant(Q=0) == -1 and _quant(sa=0) == -1
+    assert _quant(K=100) == -2 and _quant(K=0) == -2 and _quant(M=-1) == -2
+    assert _quant(dt=2) == -3 and _quant(ldx=7000) == -3 and _quant(ldx=7172) == -3
+    assert _quant(dt=1, ldx=7172) != -3  # FP32 rows need only 16-byte alignment (4 elements)
+    assert _quant(ldq=7100) == -3 and _quant(ld_sa=63) == -3 and _quant(ld_sa=66) == -3
+    assert _quant(X=(1 << 20) + 8) == -3 and _quant(Q=(1 << 20) + 4) == -3 and _quant(sa=(1 << 20) + 2) == -3
