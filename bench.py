@@ -177,9 +177,136 @@ def cpu_baseline():
                       "dense M=4096 N=4096 K=7168 shape, 240 GFLOP"}
 
 
+def grouped_work(m_live, g_active, N, K, m_padded=None):
+    """Algorithmic FLOPs and HBM bytes of one grouped call: live rows only, each active
+    group's B and sb read once, D written once for live rows."""
+    kb = K // 128
+    flops = 2.0 * m_live * N * K
+    nbytes = (m_live * K + g_active * N * K + m_live * N * 2 + m_live * kb * 4 +
+              g_active * ((N + 127) // 128) * kb * 4)
+    padded = 2.0 * m_padded * N * K if m_padded is not None else flops
+    return flops, nbytes, padded
+
+
+def grouped_bench(args):
+    """--workload grouped: the M-grouped configurations (contiguous C3, masked decode C4,
+    the MoE FFN pair C5), one step = every case once, per-case times from HIP events on
+    the launch stream. Prints one JSON line (not the default benchmark)."""
+    import torch
+    import moe_grouped_gemm_fp32_amd as fg
+    import synth
+
+    dev = torch.device("cuda:0")
+    cases = []
+
+    def add(name, fn, m_live, g_active, N, K, m_padded=None, extra=None):
+        flops, nbytes, padded = grouped_work(m_live, g_active, N, K, m_padded)
+        cases.append(dict(name=name, fn=fn, flops=flops, bytes=nbytes, padded_flops=padded, extra=extra or {}))
+
+    # C3: contiguous, groups of equal size (multiples of 128 rows: no padding rows)
+    for G, rows, N, K in ((4, 8192, 4096, 7168), (8, 4096, 7168, 2048)):
+        c = synth.contiguous_case([rows] * G, N, K, seed=3000 + G, device=dev)
+        ws = fg.make_workspace(fg.KIND_CONTIGUOUS, c["M"], N, K, G, device=dev)
+        cfg = fg.query_config(fg.KIND_CONTIGUOUS, c["M"], N, K, G)
+        add("contiguous G=%d x %d rows N=%d K=%d" % (G, rows, N, K),
+            (lambda c=c, ws=ws: fg.fp8_grouped_gemm_nt_contiguous(c["A"], c["sa"], c["B"], c["sb"], c["D"],
+                                                                  c["m_indices"], ws)),
+            G * rows, G, N, K, extra={"tile": "%dx%d" % (cfg["block_m"], cfg["block_n"]), "split_k": cfg["split_k"]})
+    # C4: masked decode, masked_m[g] uniform in [179, 333], M_max 4096, expected_m 256
+    for N, K in ((4096, 7168), (7168, 2048)):
+        for G in (1, 2, 4, 8, 16):
+            c = synth.masked_case(G, 4096, N, K, seed=4000 + G + N, device=dev, expected_m=256)
+            mm = c["masked_m_list"]
+            cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
+            add("masked G=%d N=%d K=%d" % (G, N, K),
+                (lambda c=c: fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"], c["D"],
+                                                           c["masked_m"], 256)),
+                sum(mm), sum(1 for v in mm if v > 0), N, K,
+                extra={"masked_m_sum": sum(mm), "tile": "%dx%d" % (cfg["block_m"], cfg["block_n"])})
+    # C5: MoE FFN pair over 256 experts, 4096 tokens, top-8 Zipf(1.1) routing; the
+    # down GEMM's input is the SwiGLU of the gate+up output re-quantised 1x128 (untimed glue)
+    c1 = synth.moe_case(seed=5000, device=dev, N=4096, K=7168)
+    mi = c1["m_indices"]
+    m_live = int((mi >= 0).sum())
+    g_act = sum(1 for v in c1["counts"] if v > 0)
+    ws1 = fg.make_workspace(fg.KIND_CONTIGUOUS, c1["M"], 4096, 7168, 256, device=dev)
+    fn1 = lambda: fg.fp8_grouped_gemm_nt_contiguous(c1["A"], c1["sa"], c1["B"], c1["sb"], c1["D"], mi, ws1)
+    fn1()
+    torch.cuda.synchronize()
+    A2, sa2 = synth.swiglu_requant(c1["D"].view(torch.bfloat16).float().nan_to_num(0.0), mi)
+    g2 = synth.make_generator(5001, dev)
+    B2 = torch.empty(256, 7168, 2048, dtype=torch.uint8, device=dev)
+    sb2 = torch.empty(256, 56, 16, dtype=torch.float32, device=dev)
+    for e in range(256):
+        b, sc = synth.make_weight(7168, 2048, "normal", g2, dev)
+        B2[e] = b
+        sb2[e] = sc
+    D2 = synth.sentinel_output((c1["M"], 7168), dev)
+    ws2 = fg.make_workspace(fg.KIND_CONTIGUOUS, c1["M"], 7168, 2048, 256, device=dev)
+    fn2 = lambda: fg.fp8_grouped_gemm_nt_contiguous(A2, sa2, B2, sb2, D2, mi, ws2)
+    add("moe gate+up (256 experts, %d live / %d padded rows) N=4096 K=7168" % (m_live, c1["M"]), fn1,
+        m_live, g_act, 4096, 7168, m_padded=c1["M"])
+    add("moe down (256 experts, %d live / %d padded rows) N=7168 K=2048" % (m_live, c1["M"]), fn2,
+        m_live, g_act, 7168, 2048, m_padded=c1["M"])
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, c in enumerate(cases):
+            if events is not None:
+                events[i][0].record()
+            c["fn"]()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    per = [0.0] * len(cases)
+    step()
+    all_ev = []
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
+        step(ev)
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    for ev in all_ev:
+        for i, (a, b) in enumerate(ev):
+            per[i] += a.elapsed_time(b)
+    rows, total = [], 0.0
+    for i, c in enumerate(cases):
+        ms = per[i] / args.steps
+        total += c["flops"]
+        bound, t_ideal = classify(c["flops"], c["bytes"])
+        tflops = c["flops"] / (ms * 1e-3) / 1e12
+        gbs = c["bytes"] / (ms * 1e-3) / 1e9
+        frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+        r = {"case": c["name"], "us": round(ms * 1e3, 2), "tflops": round(tflops, 1), "gbs": round(gbs, 1),
+             "bound": bound, "frac": round(frac, 4), "ideal_us": round(t_ideal * 1e6, 2),
+             "padded_tflops": round(c["padded_flops"] / (ms * 1e-3) / 1e12, 1),
+             "algo_bytes": c["bytes"], "algo_flops": c["flops"]}
+        r.update(c["extra"])
+        rows.append(r)
+    out = {"metric": METRIC, "value": round(total / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+           "data": "synthetic",
+           "config": {"workload": "M-grouped FP8 NT GEMMs: contiguous (4x8192 rows N=4096 K=7168; 8x4096 rows "
+                                  "N=7168 K=2048), masked decode (G in 1..16, M_max 4096, masked_m in [179,333]), "
+                                  "MoE FFN pair (4096 tokens, 256 experts, top-8 Zipf 1.1)"},
+           "per_case": rows}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=("dense", "grouped"), default="dense",
+                    help="dense: the 18 DeepSeek-V3-like shapes (default); grouped: contiguous, masked, MoE")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
@@ -204,6 +331,10 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported" % args.gpus}))
         sys.exit(2)
+
+    if args.workload == "grouped":
+        grouped_bench(args)
+        return
 
     import torch
     import moe_grouped_gemm_fp32_amd as fg
@@ -240,12 +371,18 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
-    # timed region 2: per-kernel durations with events on the launch stream
+    # timed region 2: per-kernel durations with events on the launch stream. One
+    # untimed step goes first and nothing synchronises until the end, so the host
+    # stays ahead of the GPU and no event pair includes host launch latency.
     per = [[0.0] for _ in cases]
+    step()
+    all_ev = []
     for _ in range(args.steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
         step(ev)
-        torch.cuda.synchronize()
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    for ev in all_ev:
         for i, (a, b) in enumerate(ev):
             per[i][0] += a.elapsed_time(b)
     traffic = {}
