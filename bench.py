@@ -126,6 +126,32 @@ def trace_summary(d, shapes):
         print(json.dumps(o))
 
 
+GROUPED_CASES = (["contiguous G=4 x 8192 rows N=4096 K=7168", "contiguous G=8 x 4096 rows N=7168 K=2048"] +
+                 ["masked G=%d N=%d K=%d" % (g, n, k) for (n, k) in ((4096, 7168), (7168, 2048)) for g in (1, 2, 4, 8, 16)] +
+                 ["moe gate+up N=4096 K=7168", "moe down N=7168 K=2048"])
+
+
+def trace_summary_grouped(d):
+    """Per-case average GEMM kernel duration of a --workload grouped run from a rocprofv3
+    --kernel-trace csv directory. The first GEMM dispatch is the untimed gate+up call that
+    produces the down GEMM's input; after it, dispatch i belongs to case i mod 14."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "fp8_gemm_kernel" in r["Kernel_Name"]:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    rows = rows[1:]
+    for i, name in enumerate(GROUPED_CASES):
+        sel = rows[i::len(GROUPED_CASES)]
+        us = sum(r[2] for r in sel) / len(sel) / 1e3
+        print(json.dumps({"case": name, "kernel": sel[0][1].replace("void fp8gemm::", ""),
+                          "dispatches": len(sel), "avg_us": round(us, 2)}))
+
+
 def copy_only(args):
     """A plain device copy of --copy-mb MiB, the calibration kernel for the byte counters."""
     import torch
@@ -322,7 +348,10 @@ def main():
         pmc_summary(args, parse_shapes(args.shapes) if args.shapes else CONFIG2)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        if args.workload == "grouped":
+            trace_summary_grouped(args.trace_summary)
+        else:
+            trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
         return
     if args.copy_mb:
         copy_only(args)
