@@ -152,6 +152,30 @@ def trace_summary_grouped(d):
                           "dispatches": len(sel), "avg_us": round(us, 2)}))
 
 
+def counter_summary(d, shapes):
+    """Per-shape mean of every counter in a rocprofv3 --pmc csv directory of the dense
+    benchmark (GEMM dispatch i belongs to shape i mod len(shapes)); values are summed
+    over the counter's hardware instances within a dispatch."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "fp8_gemm_kernel" not in r["Kernel_Name"]:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    dispatches = sorted({k[0] for k in per})
+    names = sorted({k[1] for k in per})
+    for i, (M, N, K) in enumerate(shapes):
+        sel = dispatches[i::len(shapes)]
+        row = {"M": M, "N": N, "K": K, "dispatches": len(sel)}
+        for c in names:
+            vals = [per[(x, c)] for x in sel if (x, c) in per]
+            row[c] = sum(vals) / len(vals) if vals else None
+        print(json.dumps(row))
+
+
 def copy_only(args):
     """A plain device copy of --copy-mb MiB, the calibration kernel for the byte counters."""
     import torch
@@ -340,12 +364,16 @@ def main():
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
     ap.add_argument("--copy-mb", type=int, default=0, help="only run a plain copy of this many MiB")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", help="per-shape durations from a rocprofv3 trace")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR", help="per-shape counter means from a rocprofv3 --pmc run")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="build the traffic table from rocprofv3 --pmc output directories")
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(args, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
         return
     if args.trace_summary:
         if args.workload == "grouped":
