@@ -352,11 +352,84 @@ def grouped_bench(args):
     print(json.dumps(out), flush=True)
 
 
+QUANT_CASES = [(4096, 7168, "bf16"), (4096, 2048, "bf16"), (4096, 16384, "bf16"), (32768, 7168, "bf16"),
+               (53376, 2048, "bf16"), (4096, 7168, "fp32")]
+
+
+def quant_bench(args):
+    """--workload quant: the 1x128 activation quantiser on the activation shapes that feed
+    the GEMMs (dense M=4096 at K = 7168, 2048, 16384; the MoE gate+up input of 32768
+    routed rows at K=7168; the MoE down input of 53376 padded rows at K=2048; one FP32
+    input). HBM-bound: bytes = input once + e4m3 codes + FP32 scales. One JSON line."""
+    import torch
+    import moe_grouped_gemm_fp32_amd as fg
+
+    dev = torch.device("cuda:0")
+    cases = []
+    for i, (M, K, dt) in enumerate(QUANT_CASES):
+        g = torch.Generator(device=dev)
+        g.manual_seed(7000 + i)
+        X = torch.randn(M, K, generator=g, device=dev, dtype=torch.float32)
+        if dt == "bf16":
+            X = X.to(torch.bfloat16)
+        Q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+        sa = torch.empty(K // 128, fg.scale_ld(M), dtype=torch.float32, device=dev)
+        nbytes = M * K * X.element_size() + M * K + M * (K // 128) * 4
+        cases.append(dict(name="%s %dx%d" % (dt, M, K), fn=(lambda X=X, Q=Q, sa=sa: fg.quantize_1x128(X, Q, sa)),
+                          bytes=nbytes))
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, c in enumerate(cases):
+            if events is not None:
+                events[i][0].record()
+            c["fn"]()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    step()
+    all_ev = []
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
+        step(ev)
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    per = [0.0] * len(cases)
+    for ev in all_ev:
+        for i, (a, b) in enumerate(ev):
+            per[i] += a.elapsed_time(b)
+    rows, total = [], 0
+    for i, c in enumerate(cases):
+        ms = per[i] / args.steps
+        total += c["bytes"]
+        gbs = c["bytes"] / (ms * 1e-3) / 1e9
+        rows.append({"case": c["name"], "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "ideal_us": round(c["bytes"] / PEAK_HBM_GBS / 1e3, 2),
+                     "algo_bytes": c["bytes"]})
+    out = {"metric": "1x128 activation quantisation HBM GB/s, 1xMI355X, % of HBM roofline",
+           "value": round(total / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+           "config": {"workload": "1x128 FP32-scaled e4m3 quantisation of N(0,1) activations feeding the GEMMs",
+                      "cases": [c["name"] for c in cases]},
+           "per_case": rows}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("dense", "grouped"), default="dense",
-                    help="dense: the 18 DeepSeek-V3-like shapes (default); grouped: contiguous, masked, MoE")
+    ap.add_argument("--workload", choices=("dense", "grouped", "quant"), default="dense",
+                    help="dense: the 18 DeepSeek-V3-like shapes (default); grouped: contiguous, masked, MoE; "
+                         "quant: the 1x128 activation quantiser")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
@@ -391,6 +464,9 @@ def main():
 
     if args.workload == "grouped":
         grouped_bench(args)
+        return
+    if args.workload == "quant":
+        quant_bench(args)
         return
 
     import torch
