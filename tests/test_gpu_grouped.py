@@ -192,3 +192,30 @@ def test_config5_moe_ffn_pair(cuda_device):
         b, _ = oracle.gemm_nt_sampled(A2h, sa2h, B2[e].cpu().numpy(), sb2[e].cpu().numpy(), [r], np.arange(7168))
         ref2.append(b[0])
     compare("normal", bits_of(D2)[rows], np.stack(ref2), "moe down")
+
+
+@pytest.mark.parametrize("G", [1024, 777])
+def test_masked_maximum_group_count(cuda_device, G):
+    # the largest group count the masked call accepts (the live-tile prefix sum over
+    # every group is built in LDS) and a ragged one; masked_m spans empty, partial and
+    # full groups
+    M_max, N, K = 32, 256, 256
+    rng = np.random.default_rng(G)
+    mm = rng.integers(0, M_max + 1, G)
+    mm[:3] = [0, M_max, 1]
+    c = synth.masked_case(G, M_max, N, K, seed=G, device=cuda_device, masked_m=mm.tolist(), expected_m=16)
+    ref, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm.tolist(), d_bits(c))
+    for tile in (None, (64, 64, 1), (128, 128, 1)):
+        got = bits_of(run_masked(c, tile))
+        live = np.arange(M_max)[None, :] < mm[:, None]
+        assert np.all(got[~live] == SENT), f"dead rows written (G={G}, {tile})"
+        compare("normal", got[live], ref[live], f"masked G={G} {tile}")
+
+
+def test_masked_rejects_too_many_groups():
+    # the masked call's host check: more groups than the device prefix sum holds
+    import ctypes
+    P = ctypes.c_void_p
+    st = fg.lib().fp8_grouped_gemm_nt_masked(P(1 << 20), 256, P(1 << 20), 32, P(1 << 20), 256, P(1 << 20),
+                                             P(1 << 20), 256, P(1 << 20), 1025, 32, 256, 256, 16, None, 0, None)
+    assert st == -2
