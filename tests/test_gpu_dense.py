@@ -201,3 +201,24 @@ def test_split_k_workspace_reuse_with_new_inputs(cuda_device, M, N, K, tile):
         torch.cuda.synchronize()
         ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))
         compare("e1" if call == 1 else "normal", bits_of(D)[rows], ref, f"call {call} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 384), (1000, 1000, 640), (512, 768, 128), (768, 512, 256),
+                                   (4096, 2048, 1536)])
+@pytest.mark.parametrize("kind", ["normal", "e1"])
+def test_many_tiles_per_workgroup(cuda_device, M, N, K, kind):
+    # a small grid (8 CUs) makes every workgroup run many whole tiles in a row, so each
+    # tile's first stages are loaded before the previous tile's epilogue; full and
+    # ragged (edge) tiles alternate, and K covers one to twelve 128-wide blocks
+    c = synth.dense_case(M, N, K, seed=8100 + M + N + K, device=cuda_device, kind=kind)
+    rows = sample_rows(M, 48, K) if M * N > 2_000_000 else np.arange(M)
+    ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))
+    fg.set_num_cus(8)
+    try:
+        for tile in [(256, 128, 1), (128, 256, 1), None]:
+            D, _ = run_dense(c, forced=tile)
+            got = bits_of(D)
+            assert not np.any(got == SENT), f"every output written {tile}"
+            compare(kind, got[rows], ref, f"8 CUs {tile} {M}x{N}x{K} {kind}")
+    finally:
+        fg.set_num_cus(0)
