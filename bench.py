@@ -427,9 +427,10 @@ def quant_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("dense", "grouped", "quant"), default="dense",
-                    help="dense: the 18 DeepSeek-V3-like shapes (default); grouped: contiguous, masked, MoE; "
-                         "quant: the 1x128 activation quantiser")
+    ap.add_argument("--workload", choices=("dense", "ue8m0", "grouped", "quant"), default="dense",
+                    help="dense: the 18 DeepSeek-V3-like shapes (default); ue8m0: the same shapes with "
+                         "power-of-two (UE8M0) scales through fp8_gemm_nt_ue8m0; grouped: contiguous, masked, "
+                         "MoE; quant: the 1x128 activation quantiser")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
@@ -475,9 +476,12 @@ def main():
 
     dev = torch.device("cuda:0")
     shapes = parse_shapes(args.shapes) if args.shapes else CONFIG2
+    ue8m0 = args.workload == "ue8m0"
+    gemm = fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
     cases = []
     for i, (M, N, K) in enumerate(shapes):
-        c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02)
+        c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02,
+                             kind="pow2" if ue8m0 else "normal")
         c["ws"] = fg.make_workspace(fg.KIND_DENSE, M, N, K, device=dev)
         c["cfg"] = fg.query_config(fg.KIND_DENSE, M, N, K)
         cases.append(c)
@@ -487,7 +491,7 @@ def main():
         for i, c in enumerate(cases):
             if events is not None:
                 events[i][0].record()
-            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
+            gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
             if events is not None:
                 events[i][1].record()
 
@@ -522,7 +526,7 @@ def main():
     if os.path.exists(args.traffic_file):
         with open(args.traffic_file) as f:
             tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_source_hash():  # counters of this very kernel only
+        if tr.get("kernel_sha") == kernel_source_hash() and not ue8m0:  # counters of this very kernel only
             traffic = tr.get("shapes", {})
 
     total_flops = 0.0
@@ -557,7 +561,7 @@ def main():
     roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not ue8m0:
         cpu = cpu_baseline()
 
     out = {
@@ -565,8 +569,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
         "data": "synthetic",
-        "config": {"workload": "dense FP8 NT GEMM with 1x128/128x128 FP32 scales and BF16 output over %d "
-                               "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)" % len(shapes),
+        "config": {"workload": "dense FP8 NT GEMM with 1x128/128x128 %s scales and BF16 output over %d "
+                               "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)"
+                               % ("UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes)),
                    "shapes": ["%dx%dx%d" % s for s in shapes]},
         "roofline": roof,
         "cpu_baseline": cpu,

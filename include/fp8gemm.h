@@ -93,6 +93,23 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dense NT GEMM with UE8M0 scale factors: the same operation, layouts, workspace and
+ * errors as fp8_gemm_nt, for scales that are powers of two (the UE8M0 scale format
+ * the pages list among DeepGEMM's scale-factor options: es.news.hada.io/topic?id=19459,
+ * "Interfaz GEMM y restricciones de layout"). sa and sb hold each scale as the FP32
+ * value 2^(e-127) of its E8M0 code e (1 <= e <= 254); only the exponent field is read.
+ * The kernel passes the codes to gfx950's block-scaled MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4), which scales each 128-K block product and
+ * accumulates it in FP32 itself, so no promotion FMAs run.
+ * Precondition (device data, not checked): every scale is an exact normal power of
+ * two; a mantissa would be ignored.
+ */
+int fp8_gemm_nt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const void* B, int64_t ldb, const float* sb,
+                      void* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * M-grouped contiguous GEMM (MoE training forward / inference prefill; pages:
  * es.news.hada.io/topic?id=19459 "Dense y Grouped GEMM", contiguous layout).
  * The tokens of all G experts are concatenated along M; each expert segment is

@@ -24,7 +24,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "fp8_gemm_nt", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
+    "fp8_gemm_nt", "fp8_gemm_nt_ue8m0", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
     "workspace_size", "make_workspace", "query_config", "force_config", "set_num_cus",
     "get_num_cus", "get_mk_alignment_for_contiguous_layout", "scale_ld", "num_tiles",
     "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED", "quantize_1x128",
@@ -51,6 +51,7 @@ _lib = None
 _P, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
     "fp8_gemm_nt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_nt_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked": (
@@ -153,6 +154,23 @@ def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Te
     st = lib().fp8_gemm_nt(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
                            _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt")
+    return D
+
+
+def fp8_gemm_nt_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp8_gemm_nt for UE8M0 scale factors: sa and sb (same shapes and layouts) hold
+    exact powers of two; their exponents feed the block-scaled MFMA directly."""
+    A, B, dev = _common(A, sa, B, sb, D, 0)
+    M, K = A.shape
+    N = B.shape[0]
+    _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_gemm_nt_ue8m0(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                                 _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
+    _check(st, "fp8_gemm_nt_ue8m0")
     return D
 
 

@@ -222,21 +222,24 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   return pl;
 }
 
-template <int I, bool MASKED>
+template <int I, bool MASKED, bool E8 = false>
 hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
   constexpr Variant v = kVariants[I];
-  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED>), dim3(grid),
-                     dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
+  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED, E8>),
+                     dim3(grid), dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
   return hipGetLastError();
 }
 
+// e8: power-of-two scales through the block-scaled MFMA (dense calls only)
 template <int I = 0>
-hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream) {
+hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream, bool e8) {
   if constexpr (I < kNumVariants) {
-    if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn)
+    if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn) {
+      if (e8) return launch_variant<I, false, true>(p, pl.grid, stream);
       return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true>(p, pl.grid, stream)
                                            : launch_variant<I, false>(p, pl.grid, stream);
-    return launch<I + 1>(pl, p, stream);
+    }
+    return launch<I + 1>(pl, p, stream, e8);
   } else {
     return hipErrorInvalidValue;
   }
@@ -270,7 +273,7 @@ void maybe_print(const char* what, int rows, int N, int K, int G, const Plan& pl
 }
 
 int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, int expected_m, void* workspace,
-        size_t workspace_bytes, hipStream_t stream) {
+        size_t workspace_bytes, hipStream_t stream, bool e8 = false) {
   int st;
   const int cus = effective_cus(true, &st);
   if (st != FP8GEMM_OK) return st;
@@ -299,7 +302,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
                                             (size_t)split_tiles * pl.split * pl.bm * pl.bn * sizeof(float));
   }
   if (pl.units == 0) return FP8GEMM_OK;
-  return launch(pl, p, stream) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+  return launch(pl, p, stream, e8) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 
 Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
@@ -330,6 +333,17 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
   Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
   p.M = M;
   return run(FP8GEMM_KIND_DENSE, "dense", p, M, N, K, 1, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_gemm_nt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M;
+  return run(FP8GEMM_KIND_DENSE, "dense ue8m0", p, M, N, K, 1, 0, workspace, workspace_bytes, stream, true);
 }
 
 int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,

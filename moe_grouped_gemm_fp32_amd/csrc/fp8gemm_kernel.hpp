@@ -280,7 +280,11 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
 
 // BM x BN tile, WAVES_M x WAVES_N wave64s (4 or 8), STAGES-deep LDS ring; MASKED
 // instances carry the per-group live-tile table.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED>
+// E8 instances take power-of-two scales (UE8M0 values 2^(e-127) held as FP32) and give
+// their 8-bit exponents to gfx950's block-scaled MFMA, which multiplies each 128-K
+// block product by 2^(ea-127) * 2^(eb-127) and adds it to the FP32 accumulator itself:
+// the promotion needs no separate FMAs.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED, bool E8 = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(const Params p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = NW * 64;
@@ -545,6 +549,25 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     constexpr int NMF = TM * TN;
     auto compute = [&](auto buf_c, auto&& side) {
       constexpr int buf = decltype(buf_c)::value;
+      if constexpr (E8) {
+        // scale operands: the exponent byte of each power-of-two scale (the E8M0 code);
+        // the first MFMA operand (B rows) takes the tile's weight scale, the second
+        // (A rows) the activation scale of the lane's row
+        int ea[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) ea[t] = (__float_as_int(sa_r[buf][t]) >> 23) & 0xFF;
+        const int eb = (__float_as_int(sb_r[buf]) >> 23) & 0xFF;
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+          const int t = k / TN, j = k % TN;
+          acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[buf][j], fa[buf][t], acc[t][j], 0, 0,
+                                                                       0, eb, 0, ea[t]);
+          side(k);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
       float sc[TM];
 #pragma unroll
       for (int t = 0; t < TM; ++t) sc[t] = sa_r[buf][t] * sb_r[buf];

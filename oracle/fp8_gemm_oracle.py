@@ -233,3 +233,21 @@ def quantize_1x128(x: np.ndarray):
     s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
     y = (xb / s[..., None]).astype(np.float32)
     return e4m3_rne_codes(y).reshape(R, K), np.ascontiguousarray(s.T)
+
+
+# ---------------------------------------------------------------- UE8M0 scale factors
+# An E8M0 scale code e is the power of two 2^(e - 127) (8 exponent bits, bias 127, no
+# sign and no mantissa); 255 is NaN. The pages list UE8M0 among DeepGEMM's scale
+# formats (es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout");
+# a GEMM with UE8M0 scales is the GEMM above with these values as sa and sb.
+def ue8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """E8M0 codes (uint8) -> FP64 scale values 2^(e - 127), NaN for 255."""
+    e = np.asarray(codes, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def gemm_nt_ue8m0(A, sa_codes, B, sb_codes):
+    """Dense NT GEMM with UE8M0 scale codes sa_codes [K/128, >=M], sb_codes
+    [ceil(N/128), K/128]: the definition of gemm_nt with the decoded scales."""
+    return gemm_nt(A, ue8m0_decode(sa_codes), B, ue8m0_decode(sb_codes))

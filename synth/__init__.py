@@ -20,6 +20,8 @@ Layouts produced (the library's documented layouts):
 Kinds of operand content:
   "normal": A ~ N(0, a_std), B ~ N(0, b_std), quantised with scale = amax/448
             per block (scale 1 for an all-zero block).
+  "pow2":   as "normal" with every scale rounded up to a power of two (UE8M0
+            scale factors); the e1/e2/e3 kinds below also use power-of-two scales.
   "e1":     small-integer codes {0, +-1, +-2} (A) and {0, +-1} (B), scales drawn
             from {1/2, 1, 2}; sparse enough that every output is a multiple of
             1/4 of small magnitude, so any FP32 summation order is exact and the
@@ -63,23 +65,37 @@ def _to_e4m3_bytes(x: torch.Tensor) -> torch.Tensor:
     return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def quantize_act(x: torch.Tensor, ld: Optional[int] = None):
-    """1x128 quantisation of activations x [R, K] -> (codes [R, K], sa [K/128, ld])."""
+def pow2_ceil(s: torch.Tensor) -> torch.Tensor:
+    """Smallest power of two >= s (s > 0, FP32): the UE8M0 rounding of a scale, which
+    keeps every |x / scale| within 448."""
+    m, e = torch.frexp(s)  # s = m * 2^e, 0.5 <= m < 1
+    return torch.where(m == 0.5, s, torch.ldexp(torch.ones_like(s), e))
+
+
+def _block_scale(amax: torch.Tensor, pow2: bool) -> torch.Tensor:
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    return pow2_ceil(scale) if pow2 else scale
+
+
+def quantize_act(x: torch.Tensor, ld: Optional[int] = None, pow2: bool = False):
+    """1x128 quantisation of activations x [R, K] -> (codes [R, K], sa [K/128, ld]);
+    pow2: scales rounded up to powers of two (UE8M0 scale factors)."""
     R, K = x.shape
     assert K % BLOCK_K == 0
     kb = K // BLOCK_K
     ld = scale_ld(R) if ld is None else ld
     xb = x.float().reshape(R, kb, BLOCK_K)
     amax = xb.abs().amax(dim=-1)
-    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    scale = _block_scale(amax, pow2)
     q = _to_e4m3_bytes(xb / scale.unsqueeze(-1)).reshape(R, K)
     sa = torch.zeros(kb, ld, dtype=torch.float32, device=x.device)
     sa[:, :R] = scale.t()
     return q.contiguous(), sa
 
 
-def quantize_weight(w: torch.Tensor):
-    """128x128 quantisation of weights w [N, K] -> (codes [N, K], sb [ceil(N/128), K/128])."""
+def quantize_weight(w: torch.Tensor, pow2: bool = False):
+    """128x128 quantisation of weights w [N, K] -> (codes [N, K], sb [ceil(N/128), K/128]);
+    pow2: scales rounded up to powers of two (UE8M0 scale factors)."""
     N, K = w.shape
     assert K % BLOCK_K == 0
     kb = K // BLOCK_K
@@ -88,7 +104,7 @@ def quantize_weight(w: torch.Tensor):
     wp = torch.nn.functional.pad(w.float(), (0, 0, 0, pad))
     blocks = wp.reshape(nb, BLOCK_N_SCALE, kb, BLOCK_K)
     amax = blocks.abs().amax(dim=(1, 3))
-    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    scale = _block_scale(amax, pow2)
     q = _to_e4m3_bytes(blocks / scale[:, None, :, None]).reshape(nb * BLOCK_N_SCALE, K)[:N]
     return q.contiguous(), scale.contiguous()
 
@@ -117,9 +133,9 @@ def make_act(R: int, K: int, kind: str, gen, device, std: float = 1.0, ld: Optio
     """Activation operand (codes [R, K], sa [K/128, ld]) of the given kind."""
     kb = K // BLOCK_K
     ld = scale_ld(R) if ld is None else ld
-    if kind == "normal":
+    if kind in ("normal", "pow2"):
         x = torch.randn(R, K, generator=gen, device=device, dtype=torch.float32) * std
-        return quantize_act(x, ld)
+        return quantize_act(x, ld, pow2=kind == "pow2")
     sa = torch.zeros(kb, ld, dtype=torch.float32, device=device)
     if kind == "e1":
         # density chosen so the expected |sum| over all K blocks stays near 16
@@ -145,9 +161,9 @@ def make_weight(N: int, K: int, kind: str, gen, device, std: float = 0.02):
     """Weight operand (codes [N, K], sb [ceil(N/128), K/128]) of the given kind."""
     kb = K // BLOCK_K
     nb = (N + BLOCK_N_SCALE - 1) // BLOCK_N_SCALE
-    if kind == "normal":
+    if kind in ("normal", "pow2"):
         w = torch.randn(N, K, generator=gen, device=device, dtype=torch.float32) * std
-        return quantize_weight(w)
+        return quantize_weight(w, pow2=kind == "pow2")
     if kind == "e1":
         pb = min(0.5, math.sqrt(16.0 / (1.5 * 5.44 * K)))
         q = _small_int_codes((N, K), [0, 1, -1], [1 - pb, pb / 2, pb / 2], gen, device)

@@ -151,3 +151,19 @@ def test_quantize_argument_validation_without_launch():
     assert _quant(dt=1, ldx=7172) != -3  # FP32 rows need only 16-byte alignment (4 elements)
     assert _quant(ldq=7100) == -3 and _quant(ld_sa=63) == -3 and _quant(ld_sa=66) == -3
     assert _quant(X=(1 << 20) + 8) == -3 and _quant(Q=(1 << 20) + 4) == -3 and _quant(sa=(1 << 20) + 2) == -3
+
+
+def test_ue8m0_argument_validation_without_launch():
+    L = fg.lib()
+    P = ctypes.c_void_p
+    good = dict(A=P(1 << 20), lda=512, sa=P(1 << 20), ld_sa=64, B=P(1 << 20), ldb=512, sb=P(1 << 20),
+                D=P(1 << 20), ldd=256, M=64, N=256, K=512)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.fp8_gemm_nt_ue8m0(a["A"], a["lda"], a["sa"], a["ld_sa"], a["B"], a["ldb"], a["sb"], a["D"],
+                                   a["ldd"], a["M"], a["N"], a["K"], None, 0, None)
+    assert call(A=None) == -1 and call(sb=None) == -1
+    assert call(K=100) == -2 and call(N=0) == -2
+    assert call(lda=500) == -3 and call(ld_sa=62) == -3 and call(ldd=100) == -3
+    assert call(M=0) == 0  # nothing to do, nothing launched
