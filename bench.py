@@ -248,6 +248,8 @@ def grouped_bench(args):
 
     dev = torch.device("cuda:0")
     cases = []
+    ue = bool(args.ue8m0)
+    kind = "pow2" if ue else "normal"
 
     def add(name, fn, m_live, g_active, N, K, m_padded=None, extra=None):
         flops, nbytes, padded = grouped_work(m_live, g_active, N, K, m_padded)
@@ -255,45 +257,45 @@ def grouped_bench(args):
 
     # C3: contiguous, groups of equal size (multiples of 128 rows: no padding rows)
     for G, rows, N, K in ((4, 8192, 4096, 7168), (8, 4096, 7168, 2048)):
-        c = synth.contiguous_case([rows] * G, N, K, seed=3000 + G, device=dev)
+        c = synth.contiguous_case([rows] * G, N, K, seed=3000 + G, device=dev, kind=kind)
         ws = fg.make_workspace(fg.KIND_CONTIGUOUS, c["M"], N, K, G, device=dev)
         cfg = fg.query_config(fg.KIND_CONTIGUOUS, c["M"], N, K, G)
         add("contiguous G=%d x %d rows N=%d K=%d" % (G, rows, N, K),
             (lambda c=c, ws=ws: fg.fp8_grouped_gemm_nt_contiguous(c["A"], c["sa"], c["B"], c["sb"], c["D"],
-                                                                  c["m_indices"], ws)),
+                                                                  c["m_indices"], ws, ue8m0=ue)),
             G * rows, G, N, K, extra={"tile": "%dx%d" % (cfg["block_m"], cfg["block_n"]), "split_k": cfg["split_k"]})
     # C4: masked decode, masked_m[g] uniform in [179, 333], M_max 4096, expected_m 256
     for N, K in ((4096, 7168), (7168, 2048)):
         for G in (1, 2, 4, 8, 16):
-            c = synth.masked_case(G, 4096, N, K, seed=4000 + G + N, device=dev, expected_m=256)
+            c = synth.masked_case(G, 4096, N, K, seed=4000 + G + N, device=dev, expected_m=256, kind=kind)
             mm = c["masked_m_list"]
             cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
             add("masked G=%d N=%d K=%d" % (G, N, K),
                 (lambda c=c: fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"], c["D"],
-                                                           c["masked_m"], 256)),
+                                                           c["masked_m"], 256, ue8m0=ue)),
                 sum(mm), sum(1 for v in mm if v > 0), N, K,
                 extra={"masked_m_sum": sum(mm), "tile": "%dx%d" % (cfg["block_m"], cfg["block_n"])})
     # C5: MoE FFN pair over 256 experts, 4096 tokens, top-8 Zipf(1.1) routing; the
     # down GEMM's input is the SwiGLU of the gate+up output re-quantised 1x128 (untimed glue)
-    c1 = synth.moe_case(seed=5000, device=dev, N=4096, K=7168)
+    c1 = synth.moe_case(seed=5000, device=dev, N=4096, K=7168, kind=kind)
     mi = c1["m_indices"]
     m_live = int((mi >= 0).sum())
     g_act = sum(1 for v in c1["counts"] if v > 0)
     ws1 = fg.make_workspace(fg.KIND_CONTIGUOUS, c1["M"], 4096, 7168, 256, device=dev)
-    fn1 = lambda: fg.fp8_grouped_gemm_nt_contiguous(c1["A"], c1["sa"], c1["B"], c1["sb"], c1["D"], mi, ws1)
+    fn1 = lambda: fg.fp8_grouped_gemm_nt_contiguous(c1["A"], c1["sa"], c1["B"], c1["sb"], c1["D"], mi, ws1, ue8m0=ue)
     fn1()
     torch.cuda.synchronize()
-    A2, sa2 = synth.swiglu_requant(c1["D"].view(torch.bfloat16).float().nan_to_num(0.0), mi)
+    A2, sa2 = synth.swiglu_requant(c1["D"].view(torch.bfloat16).float().nan_to_num(0.0), mi, pow2=ue)
     g2 = synth.make_generator(5001, dev)
     B2 = torch.empty(256, 7168, 2048, dtype=torch.uint8, device=dev)
     sb2 = torch.empty(256, 56, 16, dtype=torch.float32, device=dev)
     for e in range(256):
-        b, sc = synth.make_weight(7168, 2048, "normal", g2, dev)
+        b, sc = synth.make_weight(7168, 2048, kind, g2, dev)
         B2[e] = b
         sb2[e] = sc
     D2 = synth.sentinel_output((c1["M"], 7168), dev)
     ws2 = fg.make_workspace(fg.KIND_CONTIGUOUS, c1["M"], 7168, 2048, 256, device=dev)
-    fn2 = lambda: fg.fp8_grouped_gemm_nt_contiguous(A2, sa2, B2, sb2, D2, mi, ws2)
+    fn2 = lambda: fg.fp8_grouped_gemm_nt_contiguous(A2, sa2, B2, sb2, D2, mi, ws2, ue8m0=ue)
     add("moe gate+up (256 experts, %d live / %d padded rows) N=4096 K=7168" % (m_live, c1["M"]), fn1,
         m_live, g_act, 4096, 7168, m_padded=c1["M"])
     add("moe down (256 experts, %d live / %d padded rows) N=7168 K=2048" % (m_live, c1["M"]), fn2,
@@ -345,7 +347,7 @@ def grouped_bench(args):
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
            "data": "synthetic",
-           "config": {"workload": "M-grouped FP8 NT GEMMs: contiguous (4x8192 rows N=4096 K=7168; 8x4096 rows "
+           "config": {"workload": ("UE8M0-scaled " if ue else "") + "M-grouped FP8 NT GEMMs: contiguous (4x8192 rows N=4096 K=7168; 8x4096 rows "
                                   "N=7168 K=2048), masked decode (G in 1..16, M_max 4096, masked_m in [179,333]), "
                                   "MoE FFN pair (4096 tokens, 256 experts, top-8 Zipf 1.1)"},
            "per_case": rows}
@@ -435,6 +437,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ue8m0", action="store_true",
+                    help="with --workload grouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
     ap.add_argument("--copy-mb", type=int, default=0, help="only run a plain copy of this many MiB")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", help="per-shape durations from a rocprofv3 trace")

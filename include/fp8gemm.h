@@ -151,6 +151,23 @@ int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The M-grouped calls with UE8M0 scale factors: the same operations, layouts,
+ * preconditions and errors as fp8_grouped_gemm_nt_contiguous and
+ * fp8_grouped_gemm_nt_masked, with every scale an exact power of two held as FP32
+ * (see fp8_gemm_nt_ue8m0): the block-scaled MFMA applies them.
+ */
+int fp8_grouped_gemm_nt_contiguous_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                         const void* B, int64_t ldb, const float* sb,
+                                         void* D, int64_t ldd, const int32_t* m_indices,
+                                         int M_total, int N, int K, int G,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                     const void* B, int64_t ldb, const float* sb,
+                                     void* D, int64_t ldd, const int32_t* masked_m,
+                                     int G, int M_max, int N, int K, int expected_m,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * 1x128 activation quantisation: the step upstream of every call above, producing
  * the A operand and its scales (one FP32 scale per row per 128-wide K block:
  * GeekNews topic 19444, intro). The pages leave FP8 conversion to the user

@@ -56,6 +56,10 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_contiguous_ue8m0": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_masked_ue8m0": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
@@ -202,11 +206,12 @@ def quantize_1x128(X: torch.Tensor, Q: Optional[torch.Tensor] = None, sa: Option
     return Q, sa
 
 
-def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None):
+def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None, ue8m0=False):
     """M-grouped contiguous GEMM: row r of D = A[r] . B[m_indices[r]]^T; rows with -1 untouched.
 
     A [M_total, K]; sa float32 [K/128, >=M_total]; B [G, N, K]; sb [G, ceil(N/128), K/128];
     D bfloat16 [M_total, N]; m_indices int32 [M_total] on the device.
+    ue8m0: the scales are exact powers of two (fp8_grouped_gemm_nt_contiguous_ue8m0).
     """
     A, B, dev = _common(A, sa, B, sb, D, 0)
     Mt, K = A.shape
@@ -218,19 +223,22 @@ def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, s
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == Mt and m_indices.device == dev
              and m_indices.is_contiguous(), "m_indices must be a contiguous int32 [M_total] device tensor")
     wp, wb = _ws(workspace)
-    st = lib().fp8_grouped_gemm_nt_contiguous(
+    name = "fp8_grouped_gemm_nt_contiguous_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_contiguous"
+    st = getattr(lib(), name)(
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
         _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
-    _check(st, "fp8_grouped_gemm_nt_contiguous")
+    _check(st, name)
     return D
 
 
-def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, workspace=None, stream=None):
+def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, workspace=None, stream=None,
+                               ue8m0=False):
     """M-grouped masked GEMM: D[g, m] = A[g, m] . B[g]^T for m < masked_m[g]; other rows untouched.
 
     A [G, M_max, K]; sa float32 [G, K/128, ld_sa >= M_max]; B [G, N, K];
     sb [G, ceil(N/128), K/128]; D bfloat16 [G, M_max, N]; masked_m int32 [G] on
     the device (never read by the host); expected_m is a tiling hint.
+    ue8m0: the scales are exact powers of two (fp8_grouped_gemm_nt_masked_ue8m0).
     """
     A, B, dev = _common(A, sa, B, sb, D, 1)
     G, M_max, K = A.shape
@@ -244,10 +252,11 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
     _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev,
              "masked_m must be an int32 [G] device tensor")
     wp, wb = _ws(workspace)
-    st = lib().fp8_grouped_gemm_nt_masked(
+    name = "fp8_grouped_gemm_nt_masked_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_masked"
+    st = getattr(lib(), name)(
         _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
         _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
-    _check(st, "fp8_grouped_gemm_nt_masked")
+    _check(st, name)
     return D
 
 

@@ -230,12 +230,14 @@ hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// e8: power-of-two scales through the block-scaled MFMA (dense calls only)
+// e8: power-of-two scales through the block-scaled MFMA
 template <int I = 0>
 hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream, bool e8) {
   if constexpr (I < kNumVariants) {
     if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn) {
-      if (e8) return launch_variant<I, false, true>(p, pl.grid, stream);
+      if (e8)
+        return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true, true>(p, pl.grid, stream)
+                                             : launch_variant<I, false, true>(p, pl.grid, stream);
       return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true>(p, pl.grid, stream)
                                            : launch_variant<I, false>(p, pl.grid, stream);
     }
@@ -320,6 +322,45 @@ Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
   return p;
 }
 
+int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                       const float* sb, void* D, int64_t ldd, const int32_t* m_indices, int M_total, int N, int K,
+                       int G, void* workspace, size_t workspace_bytes, hipStream_t stream, bool e8) {
+  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_total, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (!m_indices) return FP8GEMM_ERR_NULL;
+  if (G <= 0) return FP8GEMM_ERR_SHAPE;
+  if (M_total == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M_total;
+  p.m_indices = m_indices;
+  p.b_gstride = (int64_t)N * ldb;
+  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  // tiles must not straddle two 128-row expert blocks
+  if (g_forced && 128 % g_forced_cfg.block_m != 0) return FP8GEMM_ERR_CONFIG;
+  return run(FP8GEMM_KIND_CONTIGUOUS, e8 ? "contiguous ue8m0" : "contiguous", p, M_total, N, K, G, 0, workspace,
+             workspace_bytes, stream, e8);
+}
+
+int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                   const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G, int M_max, int N, int K,
+                   int expected_m, hipStream_t stream, bool e8) {
+  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (!masked_m) return FP8GEMM_ERR_NULL;
+  if (G <= 0 || G > fp8gemm::kMaxGroups || M_max <= 0) return FP8GEMM_ERR_SHAPE;
+  if (g_forced && g_forced_cfg.split_k > 1) return FP8GEMM_ERR_CONFIG;  // masked never splits K
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M_max;
+  p.masked_m = masked_m;
+  p.a_gstride = (int64_t)M_max * lda;
+  p.sa_gstride = (int64_t)(K / 128) * ld_sa;
+  p.b_gstride = (int64_t)N * ldb;
+  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  p.d_gstride = (int64_t)M_max * ldd;
+  return run(FP8GEMM_KIND_MASKED, e8 ? "masked ue8m0" : "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream,
+             e8);
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,41 +391,34 @@ int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, 
                                    int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* m_indices,
                                    int M_total, int N, int K, int G, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
-  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_total, N, K);
-  if (st != FP8GEMM_OK) return st;
-  if (!m_indices) return FP8GEMM_ERR_NULL;
-  if (G <= 0) return FP8GEMM_ERR_SHAPE;
-  if (M_total == 0) return FP8GEMM_OK;
-  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
-  p.M = M_total;
-  p.m_indices = m_indices;
-  p.b_gstride = (int64_t)N * ldb;
-  p.sb_gstride = ceil_div(N, 128) * (K / 128);
-  // tiles must not straddle two 128-row expert blocks
-  if (g_forced && 128 % g_forced_cfg.block_m != 0) return FP8GEMM_ERR_CONFIG;
-  return run(FP8GEMM_KIND_CONTIGUOUS, "contiguous", p, M_total, N, K, G, 0, workspace, workspace_bytes, stream);
+  return grouped_contiguous(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, m_indices, M_total, N, K, G, workspace,
+                            workspace_bytes, stream, false);
+}
+
+int fp8_grouped_gemm_nt_contiguous_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                         int64_t ldb, const float* sb, void* D, int64_t ldd,
+                                         const int32_t* m_indices, int M_total, int N, int K, int G,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return grouped_contiguous(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, m_indices, M_total, N, K, G, workspace,
+                            workspace_bytes, stream, true);
 }
 
 int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
                                int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G,
                                int M_max, int N, int K, int expected_m, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
-  if (st != FP8GEMM_OK) return st;
-  if (!masked_m) return FP8GEMM_ERR_NULL;
-  if (G <= 0 || G > fp8gemm::kMaxGroups || M_max <= 0) return FP8GEMM_ERR_SHAPE;
-  if (g_forced && g_forced_cfg.split_k > 1) return FP8GEMM_ERR_CONFIG;  // masked never splits K
-  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
-  p.M = M_max;
-  p.masked_m = masked_m;
-  p.a_gstride = (int64_t)M_max * lda;
-  p.sa_gstride = (int64_t)(K / 128) * ld_sa;
-  p.b_gstride = (int64_t)N * ldb;
-  p.sb_gstride = ceil_div(N, 128) * (K / 128);
-  p.d_gstride = (int64_t)M_max * ldd;
   (void)workspace;
   (void)workspace_bytes;
-  return run(FP8GEMM_KIND_MASKED, "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream);
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, false);
+}
+
+int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                     int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* masked_m,
+                                     int G, int M_max, int N, int K, int expected_m, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, true);
 }
 
 int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t ldq, float* sa, int64_t ld_sa, int M,

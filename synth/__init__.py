@@ -342,7 +342,7 @@ def moe_case(seed: int, device="cpu", tokens: int = 4096, experts: int = 256, to
     if x is None:
         x = torch.randn(tokens, K, generator=gen, device=device, dtype=torch.float32)
     rows = x[tok_of_row.clamp(min=0).to(device)]
-    A, sa = quantize_act(rows)
+    A, sa = quantize_act(rows, pow2=kind == "pow2")
     live = (m_idx >= 0).to(device)
     if garbage_padding:
         A = torch.where(live[:, None], A, random_bytes((Mt, K), gen, device)).contiguous()
@@ -357,7 +357,7 @@ def moe_case(seed: int, device="cpu", tokens: int = 4096, experts: int = 256, to
                 expert_of=expert_of, D=sentinel_output((Mt, N), device))
 
 
-def swiglu_requant(h: torch.Tensor, m_indices: torch.Tensor):
+def swiglu_requant(h: torch.Tensor, m_indices: torch.Tensor, pow2: bool = False):
     """Down-projection input of the MoE FFN: SwiGLU(gate, up) of the BF16 gate+up output.
 
     h [rows, 2F] holds gate in the first F columns and up in the last F; padding
@@ -369,4 +369,4 @@ def swiglu_requant(h: torch.Tensor, m_indices: torch.Tensor):
     live = (m_indices >= 0).to(h.device)
     hf = torch.where(live[:, None], hf, torch.zeros_like(hf))
     act = torch.nn.functional.silu(hf[:, :F]) * hf[:, F:]
-    return quantize_act(act)
+    return quantize_act(act, pow2=pow2)

@@ -82,3 +82,77 @@ def test_exact_case_full_size_sampled(cuda_device):
     cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
     ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, cols)
     assert_bit_exact(got[np.ix_(rows, cols)], ref, "ue8m0 e1 4096x4096x7168")
+
+
+def _contig(c, tile, ue8m0=True):
+    D = c["D"].clone()
+    M, N, K, G = c["M"], c["N"], c["K"], c["G"]
+    nbytes = fg.workspace_size(fg.KIND_CONTIGUOUS, M, N, K, G)
+    if tile is not None and tile[2] > 1:
+        t = fg.num_tiles(M, N, tile[0], tile[1])
+        nbytes = t * tile[2] * tile[0] * tile[1] * 4 + t * 4
+    work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
+    args = (c["A"], c["sa"], c["B"], c["sb"], D, c["m_indices"], work)
+    if tile is None:
+        fg.fp8_grouped_gemm_nt_contiguous(*args, ue8m0=ue8m0)
+    else:
+        with fg.force_config(*tile):
+            fg.fp8_grouped_gemm_nt_contiguous(*args, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    return bits_of(D)
+
+
+def _masked(c, tile, ue8m0=True):
+    D = c["D"].clone()
+    args = (c["A"], c["sa"], c["B"], c["sb"], D, c["masked_m"], c["expected_m"])
+    if tile is None:
+        fg.fp8_grouped_gemm_nt_masked(*args, ue8m0=ue8m0)
+    else:
+        with fg.force_config(*tile):
+            fg.fp8_grouped_gemm_nt_masked(*args, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    return bits_of(D)
+
+
+@pytest.mark.parametrize("kind", ["pow2", "e1", "e3"])
+def test_contiguous_every_tile(cuda_device, kind):
+    c = synth.contiguous_case([5, 128, 0, 130, 1, 300], 200, 384, seed=43, device=cuda_device, kind=kind)
+    ref, _ = oracle.grouped_contiguous(*host(c, "A", "sa", "B", "sb", "m_indices"), bits_of(c["D"]))
+    pad = c["m_indices"].cpu().numpy() < 0
+    for tile in (None, (64, 64, 1), (128, 128, 1), (64, 128, 1), (128, 256, 1), (64, 64, 2), (128, 256, 2)):
+        got = _contig(c, tile)
+        assert np.all(got[pad] == SENT), f"padding rows written {tile}"
+        compare("normal" if kind == "pow2" else kind, got[~pad], ref[~pad], f"contiguous ue8m0 {kind} {tile}")
+
+
+@pytest.mark.parametrize("kind", ["pow2", "e1", "e2"])
+def test_masked_every_tile(cuda_device, kind):
+    c = synth.masked_case(5, 256, 160, 384, seed=53, device=cuda_device, masked_m=[256, 0, 1, 179, 64],
+                          kind=kind, expected_m=128)
+    ref, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), c["masked_m_list"], bits_of(c["D"]))
+    for tile in (None, (64, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1)):
+        got = _masked(c, tile)
+        for g, live in enumerate(c["masked_m_list"]):
+            assert np.all(got[g, live:] == SENT), f"dead rows of group {g} written {tile}"
+            compare("normal" if kind == "pow2" else kind, got[g, :live], ref[g, :live],
+                    f"masked ue8m0 {kind} {tile} group {g}")
+
+
+def test_grouped_full_size_sampled(cuda_device):
+    # the second contiguous configuration and a masked decode case at full size
+    c = synth.contiguous_case([4096] * 8, 7168, 2048, seed=9400, device=cuda_device, kind="pow2")
+    got = _contig(c, None)
+    assert not np.any(got == SENT)
+    rs = np.unique(np.concatenate([g * 4096 + sample_rows(4096, 2, g) for g in range(8)]))
+    ref, _ = oracle.grouped_contiguous(*host(c, "A", "sa", "B", "sb", "m_indices"), bits_of(c["D"]), rs,
+                                       np.arange(7168))
+    compare("normal", got[rs], ref, "contiguous ue8m0 8x4096 N=7168 K=2048")
+    del c, got
+    m = synth.masked_case(4, 4096, 4096, 7168, seed=9401, device=cuda_device, kind="pow2", expected_m=256)
+    got = _masked(m, None)
+    mm = m["masked_m_list"]
+    rows = [0, 1, 100, 178]
+    ref, _ = oracle.grouped_masked(*host(m, "A", "sa", "B", "sb"), mm, bits_of(m["D"]), rows, np.arange(4096))
+    compare("normal", got[:, rows], ref, "masked ue8m0 G=4 N=4096 K=7168")
+    for g, live in enumerate(mm):
+        assert np.all(got[g, live:] == SENT)
