@@ -251,3 +251,21 @@ def gemm_nt_ue8m0(A, sa_codes, B, sb_codes):
     """Dense NT GEMM with UE8M0 scale codes sa_codes [K/128, >=M], sb_codes
     [ceil(N/128), K/128]: the definition of gemm_nt with the decoded scales."""
     return gemm_nt(A, ue8m0_decode(sa_codes), B, ue8m0_decode(sb_codes))
+
+
+# ------------------------------------------------------------------ D = C + A B^T
+# The pages name the GEMMs D = C + A @ B (fp8_gemm_nt computes D = C + A @ B.T; es.news.
+# hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout"). With a BF16 D the
+# plainest reading is a BF16 C of D's shape added to the scaled sum before the one
+# rounding: D = bf16_RNE(C + S).
+def gemm_nt_c(A, sa, B, sb, C_bits, rows=None, cols=None):
+    """D = C + A B^T. C_bits: BF16 bits [M, N] (or the rows x cols subset when those are
+    given). Returns (bf16 bits, float64 C + S)."""
+    S = scaled_block_sum(A, sa, B, sb, rows, cols)
+    C = np.asarray(C_bits, dtype=np.uint16)
+    if rows is not None or cols is not None:
+        r = np.arange(C.shape[0]) if rows is None else np.asarray(rows)
+        c = np.arange(C.shape[1]) if cols is None else np.asarray(cols)
+        C = C[np.ix_(r, c)]
+    T = bf16_bits_to_f64(C) + S
+    return bf16_bits_rne(T), T
