@@ -437,6 +437,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-c", action="store_true",
+                    help="dense workload as D = C + A B^T with a BF16 C per shape (fp8_gemm_nt_c)")
     ap.add_argument("--ue8m0", action="store_true",
                     help="with --workload grouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
@@ -487,6 +489,8 @@ def main():
         c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02,
                              kind="pow2" if ue8m0 else "normal")
         c["ws"] = fg.make_workspace(fg.KIND_DENSE, M, N, K, device=dev)
+        c["C"] = (torch.randn(M, N, generator=synth.make_generator(2500 + i, dev), device=dev) * 0.1).to(
+            torch.bfloat16) if args.with_c else None
         c["cfg"] = fg.query_config(fg.KIND_DENSE, M, N, K)
         cases.append(c)
     torch.cuda.synchronize()
@@ -495,7 +499,10 @@ def main():
         for i, c in enumerate(cases):
             if events is not None:
                 events[i][0].record()
-            gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
+            if c["C"] is not None:
+                fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
+            else:
+                gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
             if events is not None:
                 events[i][1].record()
 
@@ -530,13 +537,15 @@ def main():
     if os.path.exists(args.traffic_file):
         with open(args.traffic_file) as f:
             tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_source_hash() and not ue8m0:  # counters of this very kernel only
+        if tr.get("kernel_sha") == kernel_source_hash() and not ue8m0 and not args.with_c:  # this very kernel only
             traffic = tr.get("shapes", {})
 
     total_flops = 0.0
     rows = []
     for i, ((M, N, K), c) in enumerate(zip(shapes, cases)):
         flops, nbytes = algo_work(M, N, K)
+        if args.with_c:
+            nbytes += 2 * M * N  # C read once
         total_flops += flops
         ms = per[i][0] / args.steps
         bound, t_ideal = classify(flops, nbytes)
@@ -565,7 +574,7 @@ def main():
     roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
 
     cpu = None
-    if not args.no_cpu_baseline and not ue8m0:
+    if not args.no_cpu_baseline and not ue8m0 and not args.with_c:
         cpu = cpu_baseline()
 
     out = {
@@ -575,7 +584,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense FP8 NT GEMM with 1x128/128x128 %s scales and BF16 output over %d "
                                "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)"
-                               % ("UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes)),
+                               % ("UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
+                               + (", D = C + A B^T with a BF16 C" if args.with_c else ""),
                    "shapes": ["%dx%dx%d" % s for s in shapes]},
         "roofline": roof,
         "cpu_baseline": cpu,

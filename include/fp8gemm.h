@@ -93,6 +93,33 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * D = C + A B^T (the pages' naming convention for every GEMM: fp8_gemm_nt computes
+ * D = C + A @ B.T; es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de
+ * layout"). The three calls below are fp8_gemm_nt, fp8_grouped_gemm_nt_contiguous and
+ * fp8_grouped_gemm_nt_masked with an optional addend:
+ *   C  bf16 with D's shape and layout conventions (row stride ldc >= N, 2-byte aligned;
+ *      masked: [G, M_max, N] with group stride M_max * ldc), read only where D is
+ *      written; D = bf16_rne(C + the FP32 accumulation). C == NULL is the plain call.
+ *      C may be D itself (in-place accumulation: each element is read before it is
+ *      written, by the same lane); other overlaps of C and D are undefined.
+ * Errors as for the plain calls, plus FP8GEMM_ERR_LAYOUT for ldc < N or a misaligned C.
+ */
+int fp8_gemm_nt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                  const void* B, int64_t ldb, const float* sb,
+                  const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fp8_grouped_gemm_nt_contiguous_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                     const void* B, int64_t ldb, const float* sb,
+                                     const void* C, int64_t ldc, void* D, int64_t ldd,
+                                     const int32_t* m_indices, int M_total, int N, int K, int G,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fp8_grouped_gemm_nt_masked_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                 const void* B, int64_t ldb, const float* sb,
+                                 const void* C, int64_t ldc, void* D, int64_t ldd,
+                                 const int32_t* masked_m, int G, int M_max, int N, int K, int expected_m,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Dense NT GEMM with UE8M0 scale factors: the same operation, layouts, workspace and
  * errors as fp8_gemm_nt, for scales that are powers of two (the UE8M0 scale format
  * the pages list among DeepGEMM's scale-factor options: es.news.hada.io/topic?id=19459,

@@ -52,6 +52,12 @@ _P, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_si
 _SIGS = {
     "fp8_gemm_nt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_gemm_nt_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_nt_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_contiguous_c": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_masked_c": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ,
+               _P]),
     "fp8_grouped_gemm_nt_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked": (
@@ -139,14 +145,22 @@ def _common(A, sa, B, sb, D, rows_dim):
     return A, B, dev
 
 
+def _check_c(C, D):
+    """The optional addend of D = C + A B^T: bfloat16 with D's shape, unit inner stride,
+    on D's device (it may be D itself)."""
+    _require(C.dtype == torch.bfloat16 and tuple(C.shape) == tuple(D.shape) and C.device == D.device
+             and C.stride(-1) == 1, "C must be bfloat16 with D's shape and a unit inner stride")
+
+
 def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None, stream=None, C: Optional[torch.Tensor] = None) -> torch.Tensor:
     """D[M, N] = A[M, K] . B[N, K]^T with 1x128 (sa [K/128, ld_sa]) and 128x128 (sb) scales.
 
     A, B: e4m3 bytes (uint8 or float8_e4m3fn), row-major with unit inner stride.
     sa: float32 [K/128, ld_sa], row stride ld_sa >= M. sb: float32 [ceil(N/128), K/128].
     D: bfloat16 [M, N] (written in place and returned). workspace: optional
     zero-initialised uint8 device buffer enabling split-K (see make_workspace).
+    C: optional bfloat16 addend, D = C + A B^T (fp8_gemm_nt_c); may be D itself.
     """
     A, B, dev = _common(A, sa, B, sb, D, 0)
     M, K = A.shape
@@ -155,6 +169,12 @@ def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Te
     _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
     _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
     wp, wb = _ws(workspace)
+    if C is not None:
+        _check_c(C, D)
+        st = lib().fp8_gemm_nt_c(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                                 _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
+        _check(st, "fp8_gemm_nt_c")
+        return D
     st = lib().fp8_gemm_nt(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
                            _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt")
@@ -206,12 +226,13 @@ def quantize_1x128(X: torch.Tensor, Q: Optional[torch.Tensor] = None, sa: Option
     return Q, sa
 
 
-def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None, ue8m0=False):
+def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, stream=None, ue8m0=False, C=None):
     """M-grouped contiguous GEMM: row r of D = A[r] . B[m_indices[r]]^T; rows with -1 untouched.
 
     A [M_total, K]; sa float32 [K/128, >=M_total]; B [G, N, K]; sb [G, ceil(N/128), K/128];
     D bfloat16 [M_total, N]; m_indices int32 [M_total] on the device.
     ue8m0: the scales are exact powers of two (fp8_grouped_gemm_nt_contiguous_ue8m0).
+    C: optional bfloat16 addend [M_total, N], D = C + A B^T on live rows (..._contiguous_c).
     """
     A, B, dev = _common(A, sa, B, sb, D, 0)
     Mt, K = A.shape
@@ -223,6 +244,14 @@ def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, s
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == Mt and m_indices.device == dev
              and m_indices.is_contiguous(), "m_indices must be a contiguous int32 [M_total] device tensor")
     wp, wb = _ws(workspace)
+    if C is not None:
+        _require(not ue8m0, "C is supported with FP32 scales")
+        _check_c(C, D)
+        st = lib().fp8_grouped_gemm_nt_contiguous_c(
+            _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(0),
+            _ptr(D), D.stride(0), _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
+        _check(st, "fp8_grouped_gemm_nt_contiguous_c")
+        return D
     name = "fp8_grouped_gemm_nt_contiguous_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_contiguous"
     st = getattr(lib(), name)(
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
@@ -232,13 +261,14 @@ def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, s
 
 
 def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, workspace=None, stream=None,
-                               ue8m0=False):
+                               ue8m0=False, C=None):
     """M-grouped masked GEMM: D[g, m] = A[g, m] . B[g]^T for m < masked_m[g]; other rows untouched.
 
     A [G, M_max, K]; sa float32 [G, K/128, ld_sa >= M_max]; B [G, N, K];
     sb [G, ceil(N/128), K/128]; D bfloat16 [G, M_max, N]; masked_m int32 [G] on
     the device (never read by the host); expected_m is a tiling hint.
     ue8m0: the scales are exact powers of two (fp8_grouped_gemm_nt_masked_ue8m0).
+    C: optional bfloat16 addend [G, M_max, N] (contiguous), D = C + A B^T on live rows.
     """
     A, B, dev = _common(A, sa, B, sb, D, 1)
     G, M_max, K = A.shape
@@ -252,6 +282,15 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
     _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev,
              "masked_m must be an int32 [G] device tensor")
     wp, wb = _ws(workspace)
+    if C is not None:
+        _require(not ue8m0, "C is supported with FP32 scales")
+        _check_c(C, D)
+        _require(C.is_contiguous(), "C must be contiguous")
+        st = lib().fp8_grouped_gemm_nt_masked_c(
+            _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(1),
+            _ptr(D), D.stride(1), _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
+        _check(st, "fp8_grouped_gemm_nt_masked_c")
+        return D
     name = "fp8_grouped_gemm_nt_masked_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_masked"
     st = getattr(lib(), name)(
         _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),

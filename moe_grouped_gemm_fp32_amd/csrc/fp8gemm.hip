@@ -222,10 +222,10 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   return pl;
 }
 
-template <int I, bool MASKED, bool E8 = false>
+template <int I, bool MASKED, bool E8 = false, bool HAS_C = false>
 hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
   constexpr Variant v = kVariants[I];
-  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED, E8>),
+  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED, E8, HAS_C>),
                      dim3(grid), dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -238,6 +238,9 @@ hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream, bool e8) 
       if (e8)
         return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true, true>(p, pl.grid, stream)
                                              : launch_variant<I, false, true>(p, pl.grid, stream);
+      if (p.C)  // D = C + A B^T (FP32 scales)
+        return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true, false, true>(p, pl.grid, stream)
+                                             : launch_variant<I, false, false, true>(p, pl.grid, stream);
       return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true>(p, pl.grid, stream)
                                            : launch_variant<I, false>(p, pl.grid, stream);
     }
@@ -261,6 +264,13 @@ int check_common(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   // the kernels address rows of one operand (one group) with 32-bit byte offsets
   if ((int64_t)std::max(rows - 1, 0) * lda + K > (int64_t)UINT32_MAX) return FP8GEMM_ERR_SHAPE;
   if ((int64_t)(N - 1) * ldb + K > (int64_t)UINT32_MAX) return FP8GEMM_ERR_SHAPE;
+  return FP8GEMM_OK;
+}
+
+// optional addend C (BF16, D's shape): row stride and element alignment
+int check_c(const void* C, int64_t ldc, int N) {
+  if (!C) return FP8GEMM_OK;
+  if (ldc < N || !aligned(C, 2)) return FP8GEMM_ERR_LAYOUT;
   return FP8GEMM_OK;
 }
 
@@ -297,6 +307,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.full_tiles = (int)pl.full;
   p.group_m = 8;
   p.vec_store = (p.ldd % 8 == 0 && aligned(p.D, 16)) ? 2 : (p.ldd % 4 == 0 && aligned(p.D, 8)) ? 1 : 0;
+  p.c_vec = p.C && p.ldc % 8 == 0 && aligned(p.C, 16) ? 1 : 0;
   if (pl.split > 1) {
     const int64_t split_tiles = (pl.units - pl.full) / pl.split;
     p.ws = static_cast<float*>(workspace);
@@ -324,8 +335,10 @@ Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
 
 int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                        const float* sb, void* D, int64_t ldd, const int32_t* m_indices, int M_total, int N, int K,
-                       int G, void* workspace, size_t workspace_bytes, hipStream_t stream, bool e8) {
+                       int G, void* workspace, size_t workspace_bytes, hipStream_t stream, bool e8,
+                       const void* C = nullptr, int64_t ldc = 0) {
   int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_total, N, K);
+  if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
   if (st != FP8GEMM_OK) return st;
   if (!m_indices) return FP8GEMM_ERR_NULL;
   if (G <= 0) return FP8GEMM_ERR_SHAPE;
@@ -333,6 +346,8 @@ int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_s
   Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
   p.M = M_total;
   p.m_indices = m_indices;
+  p.C = static_cast<const uint16_t*>(C);
+  p.ldc = ldc;
   p.b_gstride = (int64_t)N * ldb;
   p.sb_gstride = ceil_div(N, 128) * (K / 128);
   // tiles must not straddle two 128-row expert blocks
@@ -343,8 +358,9 @@ int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_s
 
 int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                    const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G, int M_max, int N, int K,
-                   int expected_m, hipStream_t stream, bool e8) {
+                   int expected_m, hipStream_t stream, bool e8, const void* C = nullptr, int64_t ldc = 0) {
   int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
+  if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
   if (st != FP8GEMM_OK) return st;
   if (!masked_m) return FP8GEMM_ERR_NULL;
   if (G <= 0 || G > fp8gemm::kMaxGroups || M_max <= 0) return FP8GEMM_ERR_SHAPE;
@@ -357,6 +373,9 @@ int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
   p.b_gstride = (int64_t)N * ldb;
   p.sb_gstride = ceil_div(N, 128) * (K / 128);
   p.d_gstride = (int64_t)M_max * ldd;
+  p.C = static_cast<const uint16_t*>(C);
+  p.ldc = ldc;
+  p.c_gstride = (int64_t)M_max * ldc;
   return run(FP8GEMM_KIND_MASKED, e8 ? "masked ue8m0" : "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream,
              e8);
 }
@@ -374,6 +393,20 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
   Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
   p.M = M;
   return run(FP8GEMM_KIND_DENSE, "dense", p, M, N, K, 1, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_gemm_nt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                  const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K);
+  if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M;
+  p.C = static_cast<const uint16_t*>(C);
+  p.ldc = ldc;
+  return run(FP8GEMM_KIND_DENSE, C ? "dense +C" : "dense", p, M, N, K, 1, 0, workspace, workspace_bytes, stream);
 }
 
 int fp8_gemm_nt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
@@ -401,6 +434,24 @@ int fp8_grouped_gemm_nt_contiguous_ue8m0(const void* A, int64_t lda, const float
                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return grouped_contiguous(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, m_indices, M_total, N, K, G, workspace,
                             workspace_bytes, stream, true);
+}
+
+int fp8_grouped_gemm_nt_contiguous_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                     int64_t ldb, const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd,
+                                     const int32_t* m_indices, int M_total, int N, int K, int G, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return grouped_contiguous(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, m_indices, M_total, N, K, G, workspace,
+                            workspace_bytes, stream, false, C, ldc);
+}
+
+int fp8_grouped_gemm_nt_masked_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                 int64_t ldb, const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd,
+                                 const int32_t* masked_m, int G, int M_max, int N, int K, int expected_m,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, false,
+                        C, ldc);
 }
 
 int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,

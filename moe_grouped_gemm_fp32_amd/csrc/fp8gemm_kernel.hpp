@@ -61,6 +61,9 @@ struct Params {
   int group_m;               // raster group height in tiles
   int vec_store;             // widest D store: 2 = 16 bytes (ldd % 8 == 0, D 16-byte aligned),
                              // 1 = 8 bytes (ldd % 4 == 0, D 8-byte aligned), 0 = 2 bytes
+  const uint16_t* C;         // optional BF16 addend of D = C + A B^T (nullptr: none); may alias D
+  int64_t ldc, c_gstride;    // C row stride, per-group stride (masked)
+  int c_vec;                 // 1: C rows allow 16-byte loads (ldc % 8 == 0, C 16-byte aligned)
   float* ws;                 // split-K partials [split tile][split][BM*BN]
   int32_t* counters;         // split-K arrival counters [split tile]
 };
@@ -92,6 +95,28 @@ __device__ __forceinline__ void store_edge(uint16_t* dst, uint4 w, int left, int
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       if (c < left) dst[c] = (uint16_t)(d[c >> 1] >> (16 * (c & 1)));
+  }
+}
+
+// D = C + A B^T: add the BF16 addend of eight consecutive output columns (the lane's
+// u = columns 0..3, v = columns 4..7) of which only the first `left` exist; `vec` allows
+// one 16-byte load. Each lane reads only the C elements of the D elements it writes, so
+// C may be D itself.
+__device__ __forceinline__ float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ void add_c(v4f& u, v4f& v, const uint16_t* src, int left, int vec) {
+  if (left >= 8 && vec) {
+    const uint4 c = *reinterpret_cast<const uint4*>(src);
+    u[0] += bf16_value(c.x & 0xFFFF), u[1] += bf16_value(c.x >> 16);
+    u[2] += bf16_value(c.y & 0xFFFF), u[3] += bf16_value(c.y >> 16);
+    v[0] += bf16_value(c.z & 0xFFFF), v[1] += bf16_value(c.z >> 16);
+    v[2] += bf16_value(c.w & 0xFFFF), v[3] += bf16_value(c.w >> 16);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c < left) u[c] += bf16_value(src[c]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c + 4 < left) v[c] += bf16_value(src[c + 4]);
   }
 }
 
@@ -284,7 +309,8 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
 // their 8-bit exponents to gfx950's block-scaled MFMA, which multiplies each 128-K
 // block product by 2^(ea-127) * 2^(eb-127) and adds it to the FP32 accumulator itself:
 // the promotion needs no separate FMAs.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED, bool E8 = false>
+// HAS_C instances add the BF16 C of D = C + A B^T in the epilogue (p.C non-null).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED, bool E8 = false, bool HAS_C = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(const Params p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = NW * 64;
@@ -751,26 +777,77 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     // ---- epilogue: BF16 round-to-nearest-even, live rows only; subtiles 2h and 2h+1
     // of a lane are eight consecutive columns (b_col)
     uint16_t* Dg = p.D + (MASKED ? (int64_t)g * p.d_gstride : 0);
+    const uint16_t* Cg = HAS_C ? p.C + (MASKED ? (int64_t)g * p.c_gstride : 0) : nullptr;
     int live_rows = p.M;
     if (MASKED) live_rows = min(max(p.masked_m[g], 0), p.M);
     const bool full = p.vec_store == 2 && n0 + BN <= p.N;  // no column edge in this tile
     const int ncol = n0 + wn * WTN + 8 * (lane >> 4);
+    if constexpr (HAS_C) {
+      bool okv[TM];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const int m = m0 + wm * WTM + 16 * t + (lane & 15);
-      bool ok = m < live_rows;
-      if (ok && p.kind == kContiguous) ok = p.m_indices[m] >= 0;
-      if (!ok) continue;
-      uint16_t* drow = Dg + (int64_t)m * p.ldd + ncol;
+      for (int t = 0; t < TM; ++t) {
+        const int m = m0 + wm * WTM + 16 * t + (lane & 15);
+        bool ok = m < live_rows;
+        if (ok && p.kind == kContiguous) ok = p.m_indices[m] >= 0;
+        okv[t] = ok;
+      }
+      // a lane issues all of its 16-byte C loads before any of its stores (C may be D,
+      // so the compiler would otherwise keep each load behind the previous store); edge
+      // tiles and unaligned C load element by element in add_c
+      const bool cfast = full && p.c_vec;
+      uint4 cv[TM][TN / 2];
+      if (cfast) {
 #pragma unroll
-      for (int h = 0; h < TN / 2; ++h) {
-        const v4f u = acc[t][2 * h], v = acc[t][2 * h + 1];
-        const uint4 w = make_uint4(bf16x2_bits(u[0], u[1]), bf16x2_bits(u[2], u[3]), bf16x2_bits(v[0], v[1]),
-                                   bf16x2_bits(v[2], v[3]));
-        if (full)
-          *reinterpret_cast<uint4*>(drow + 32 * h) = w;
-        else
-          store_edge(drow + 32 * h, w, p.N - (ncol + 32 * h), p.vec_store);
+        for (int t = 0; t < TM; ++t)
+          if (okv[t]) {
+            const uint16_t* crow = Cg + (int64_t)(m0 + wm * WTM + 16 * t + (lane & 15)) * p.ldc + ncol;
+#pragma unroll
+            for (int h = 0; h < TN / 2; ++h) cv[t][h] = *reinterpret_cast<const uint4*>(crow + 32 * h);
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int m = m0 + wm * WTM + 16 * t + (lane & 15);
+        if (!okv[t]) continue;
+        uint16_t* drow = Dg + (int64_t)m * p.ldd + ncol;
+#pragma unroll
+        for (int h = 0; h < TN / 2; ++h) {
+          v4f u = acc[t][2 * h], v = acc[t][2 * h + 1];
+          if (cfast) {
+            const uint4 c = cv[t][h];
+            u[0] += bf16_value(c.x & 0xFFFF), u[1] += bf16_value(c.x >> 16);
+            u[2] += bf16_value(c.y & 0xFFFF), u[3] += bf16_value(c.y >> 16);
+            v[0] += bf16_value(c.z & 0xFFFF), v[1] += bf16_value(c.z >> 16);
+            v[2] += bf16_value(c.w & 0xFFFF), v[3] += bf16_value(c.w >> 16);
+          } else {
+            add_c(u, v, Cg + (int64_t)m * p.ldc + ncol + 32 * h, p.N - (ncol + 32 * h), p.c_vec);
+          }
+          const uint4 w = make_uint4(bf16x2_bits(u[0], u[1]), bf16x2_bits(u[2], u[3]), bf16x2_bits(v[0], v[1]),
+                                     bf16x2_bits(v[2], v[3]));
+          if (full)
+            *reinterpret_cast<uint4*>(drow + 32 * h) = w;
+          else
+            store_edge(drow + 32 * h, w, p.N - (ncol + 32 * h), p.vec_store);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int m = m0 + wm * WTM + 16 * t + (lane & 15);
+        bool ok = m < live_rows;
+        if (ok && p.kind == kContiguous) ok = p.m_indices[m] >= 0;
+        if (!ok) continue;
+        uint16_t* drow = Dg + (int64_t)m * p.ldd + ncol;
+#pragma unroll
+        for (int h = 0; h < TN / 2; ++h) {
+          const v4f u = acc[t][2 * h], v = acc[t][2 * h + 1];
+          const uint4 w = make_uint4(bf16x2_bits(u[0], u[1]), bf16x2_bits(u[2], u[3]), bf16x2_bits(v[0], v[1]),
+                                     bf16x2_bits(v[2], v[3]));
+          if (full)
+            *reinterpret_cast<uint4*>(drow + 32 * h) = w;
+          else
+            store_edge(drow + 32 * h, w, p.N - (ncol + 32 * h), p.vec_store);
+        }
       }
     }
   }

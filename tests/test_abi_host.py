@@ -167,3 +167,17 @@ def test_ue8m0_argument_validation_without_launch():
     assert call(K=100) == -2 and call(N=0) == -2
     assert call(lda=500) == -3 and call(ld_sa=62) == -3 and call(ldd=100) == -3
     assert call(M=0) == 0  # nothing to do, nothing launched
+
+
+def test_c_argument_validation_without_launch():
+    L = fg.lib()
+    P = ctypes.c_void_p
+
+    def call(C=P(1 << 20), ldc=256):
+        return L.fp8_gemm_nt_c(P(1 << 20), 512, P(1 << 20), 64, P(1 << 20), 512, P(1 << 20), C, ldc, P(1 << 20),
+                               256, 64, 256, 512, None, 0, None)
+    assert call(ldc=255) == -3                   # ldc < N
+    assert call(C=P((1 << 20) + 1)) == -3        # not 2-byte aligned
+    st = L.fp8_gemm_nt_c(P(1 << 20), 512, P(1 << 20), 64, P(1 << 20), 512, P(1 << 20), P(1 << 20), 256,
+                         P(1 << 20), 256, 0, 256, 512, None, 0, None)
+    assert st == 0                               # M == 0: nothing to do
