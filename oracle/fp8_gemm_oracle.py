@@ -29,6 +29,9 @@ Grouped variants ("Dense y Grouped GEMM", es.news.hada.io/topic?id=19459):
                 m_indices[r]; rows with -1 are padding and keep their old output.
   masked     -- A is [G, M_max, K]; only the first masked_m[g] rows of group g are
                 computed, the rest keep their old output.
+  K-grouped  -- the weight-gradient form D[g] = C[g] + A_g^T B_g, A [K, M] and B [K, N]
+                split along K into per-expert segments, FP32 output (k_grouped_tn;
+                its readings are stated beside it).
 
 Every function below is pinned by tests/test_oracle_*.py (brute force in exact
 rationals, bit-exact integer cases, a closed-form scale-indexing probe, library
@@ -269,3 +272,64 @@ def gemm_nt_c(A, sa, B, sb, C_bits, rows=None, cols=None):
         C = C[np.ix_(r, c)]
     T = bf16_bits_to_f64(C) + S
     return bf16_bits_rne(T), T
+
+
+# ------------------------------------------------------ K-grouped TN (weight gradient)
+# The pages name a K-grouped contiguous GEMM for the MoE weight-gradient backward:
+# M and N fixed, the reduction axis K split into per-expert segments laid end to end
+# (k_grouped_fp8_gemm_tn_contiguous; es.news.hada.io/topic?id=19459, "Dense y Grouped
+# GEMM"). "TN" is the layout pair of D = A^T B: A stored [K, M] and B stored [K, N],
+# K the outer (strided) axis of both ("Interfaz GEMM y restricciones de layout").
+# Readings (the pages give no more): each segment's length is a multiple of 128 (the
+# alignment of the contiguous layouts); both operands are token-axis activations, so
+# each carries one FP32 scale per column per 128-long K block (sa [K/128, M],
+# sb [K/128, N]); the output is one FP32 matrix per group, D[g] = C[g] + sum, rounded
+# once to FP32, where C[g] is the old D[g] when accumulating and +0 otherwise.
+def k_grouped_tn_sum(A, sa, B, sb, k_start, k_len, rows=None, cols=None):
+    """S[m, n] = sum over the 128-blocks kb of [k_start, k_start + k_len) of
+    P_kb[m, n] * sa[kb, m] * sb[kb, n], P_kb[m, n] = sum_{k in kb} A[k, m] B[k, n] (FP64;
+    every P_kb exact). A uint8 [K, M], sa [K/128, >=M], B uint8 [K, N], sb [K/128, >=N]."""
+    A = np.asarray(A, dtype=np.uint8)
+    B = np.asarray(B, dtype=np.uint8)
+    assert k_start % BLOCK == 0 and k_len % BLOCK == 0
+    rows = np.arange(A.shape[1]) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(B.shape[1]) if cols is None else np.asarray(cols, dtype=np.int64)
+    sa = np.asarray(sa, dtype=np.float32)
+    sb = np.asarray(sb, dtype=np.float32)
+    S = np.zeros((len(rows), len(cols)), dtype=np.float64)
+    for k0 in range(k_start, k_start + k_len, BLOCK):
+        kb = k0 // BLOCK
+        a = decode_e4m3(A[k0:k0 + BLOCK][:, rows])        # [128, m]
+        b = decode_e4m3(B[k0:k0 + BLOCK][:, cols])        # [128, n]
+        P = a.T @ b                                       # exact block partial
+        s = sa[kb, rows].astype(np.float64)[:, None] * sb[kb, cols].astype(np.float64)[None, :]
+        S += P * s
+    return S
+
+
+def k_grouped_tn(A, sa, B, sb, ks, D_in=None, rows=None, cols=None):
+    """K-grouped TN GEMM: group g covers K rows [sum(ks[:g]), sum(ks[:g+1])).
+    D_in: FP32 [G, M, N] (or [G, rows, cols] with a subset) added when accumulating.
+    Returns (FP32 [G, ., .], FP64 C + S [G, ., .])."""
+    starts = np.concatenate([[0], np.cumsum(np.asarray(ks, dtype=np.int64))])
+    T = []
+    for g, k_len in enumerate(ks):
+        S = k_grouped_tn_sum(A, sa, B, sb, int(starts[g]), int(k_len), rows, cols)
+        if D_in is not None:
+            S = np.asarray(D_in[g], dtype=np.float32).astype(np.float64) + S
+        T.append(S)
+    T = np.stack(T) if T else np.zeros((0, 0, 0))
+    return T.astype(np.float32), T           # float64 -> float32 rounds to nearest even
+
+
+def k_grouped_tn_abs(A, sa, B, sb, ks, rows=None, cols=None):
+    """sum_kb |s_kb| sum_k |A B|: the magnitude that bounds the rounding error of any
+    FP32 evaluation of k_grouped_tn (same shapes as its result)."""
+    a = E4M3_TABLE_ABS_CODES[np.asarray(A, dtype=np.uint8)]
+    b = E4M3_TABLE_ABS_CODES[np.asarray(B, dtype=np.uint8)]
+    return k_grouped_tn(a, np.abs(np.asarray(sa, np.float32)), b, np.abs(np.asarray(sb, np.float32)),
+                        ks, None, rows, cols)[1]
+
+
+# code of |value| for every e4m3 code (sign bit cleared; NaN codes kept)
+E4M3_TABLE_ABS_CODES = (np.arange(256) & 0x7F).astype(np.uint8)

@@ -370,3 +370,38 @@ def swiglu_requant(h: torch.Tensor, m_indices: torch.Tensor, pow2: bool = False)
     hf = torch.where(live[:, None], hf, torch.zeros_like(hf))
     act = torch.nn.functional.silu(hf[:, :F]) * hf[:, F:]
     return quantize_act(act, pow2=pow2)
+
+
+# --------------------------------------------------------------- K-grouped (TN) inputs
+def k_grouped_case(tokens: Sequence[int], M: int, N: int, seed: int, device="cpu",
+                   kind: str = "normal", a_std: float = 1.0, b_std: float = 1.0,
+                   lda: Optional[int] = None, ldb: Optional[int] = None) -> Dict[str, object]:
+    """Inputs of the K-grouped TN GEMM (MoE weight gradient): group g's segment holds
+    tokens[g] token rows padded with zero rows to a multiple of 128 (ks[g]); the
+    segments are laid end to end along K. Both operands are token-major activations,
+    quantised per column per 128-row block: A codes [K, lda] with scales sa [K/128,
+    scale_ld(M)], B codes [K, ldb] with sb [K/128, scale_ld(N)] (columns past M / N of
+    the code arrays hold random bytes). D is FP32 [G, M, N] filled with NaN."""
+    gen = make_generator(seed, device)
+    ks = [(int(t) + BLOCK_K - 1) // BLOCK_K * BLOCK_K for t in tokens]
+    K = sum(ks)
+    lda = M if lda is None else lda
+    ldb = N if ldb is None else ldb
+    live = torch.zeros(K, dtype=torch.bool, device=device)
+    k0 = 0
+    for t, k in zip(tokens, ks):
+        live[k0:k0 + int(t)] = True
+        k0 += k
+
+    def operand(C, ld, std):
+        q, s = make_act(C, K, kind, gen, device, std=std)      # [C, K], [K/128, scale_ld(C)]
+        q = torch.where(live[None, :], q, torch.zeros_like(q))
+        full = random_bytes((K, ld), gen, device)
+        full[:, :C] = q.t()
+        return full.contiguous(), s
+
+    A, sa = operand(M, lda, a_std)
+    B, sb = operand(N, ldb, b_std)
+    D = torch.full((len(ks), M, N), float("nan"), dtype=torch.float32, device=device)
+    return dict(kind="k_grouped", M=M, N=N, K=K, G=len(ks), ks=ks, tokens=list(tokens),
+                A=A, sa=sa, B=B, sb=sb, lda=lda, ldb=ldb, D=D)
