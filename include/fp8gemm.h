@@ -195,6 +195,42 @@ int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * K-grouped TN GEMM, the MoE weight-gradient form: grouping along K with M and N
+ * fixed (es.news.hada.io/topic?id=19459, "Dense y Grouped GEMM",
+ * k_grouped_fp8_gemm_tn_contiguous; "TN" is the layout pair of D = A^T B, "Interfaz
+ * GEMM y restricciones de layout"). Group g owns the K rows [k_g, k_g + ks[g]),
+ * k_g = ks[0] + ... + ks[g-1], of both operands, and
+ *   D[g][m][n] = (accumulate ? D[g][m][n] : 0)
+ *                + sum over the 128-row blocks kb of group g of
+ *                  P_kb[m][n] * sa[kb][m] * sb[kb][n],   P_kb = sum_k A[k][m] B[k][n],
+ * accumulated in FP32 (the scaled block partials added one by one). The pages give no
+ * scale granularity or output type for this call; the reading implemented: both
+ * operands are token-axis activations quantised per column per 128 K rows, and the
+ * output is FP32 (weight gradients), optionally accumulated.
+ *   A   e4m3 [K][M] (K = sum of ks), row stride lda bytes: lda >= M, lda % 16 == 0,
+ *       16-byte aligned, lda <= 2^26. Bytes in columns M..lda-1 are read but unused.
+ *   sa  fp32 [K/128][ld_sa]: sa[kb * ld_sa + m], ld_sa >= M, 4-byte aligned.
+ *   B   e4m3 [K][N], row stride ldb: as A with N.
+ *   sb  fp32 [K/128][ld_sb]: sb[kb * ld_sb + n], ld_sb >= N.
+ *   D   fp32 [G][M][N]: D[g * d_gstride + m * ldd + n], ldd >= N, 4-byte aligned;
+ *       d_gstride >= (M - 1) * ldd + N when G > 1. Elements outside the G x M x N
+ *       box are not touched.
+ *   ks  HOST array of G group lengths in K rows, each >= 0 and a multiple of 128
+ *       (fp8_gemm_get_mk_alignment_for_contiguous_layout); a group with ks[g] == 0
+ *       writes D[g] = 0 (or leaves it unchanged when accumulating).
+ *   G   1 .. 256 groups; M, N >= 1; K <= 2^31 - 1.
+ * Device pointers are owned by the caller; ks is read before the call returns; the
+ * work is enqueued on `stream`. Errors: FP8GEMM_ERR_NULL, _SHAPE (G, M, N out of
+ * range, a group length that is negative or not a multiple of 128), _LAYOUT (strides,
+ * alignment), _DEVICE, _LAUNCH; nothing is launched on an argument error.
+ */
+int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                     const void* B, int64_t ldb, const float* sb, int64_t ld_sb,
+                                     float* D, int64_t ldd, int64_t d_gstride,
+                                     const int32_t* ks, int G, int M, int N, int accumulate,
+                                     hipStream_t stream);
+
+/*
  * 1x128 activation quantisation: the step upstream of every call above, producing
  * the A operand and its scales (one FP32 scale per row per 128-wide K block:
  * GeekNews topic 19444, intro). The pages leave FP8 conversion to the user

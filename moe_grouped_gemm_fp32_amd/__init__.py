@@ -66,6 +66,8 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked_ue8m0": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_k_grouped_gemm_tn_contiguous": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
@@ -296,6 +298,42 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
         _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
         _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
     _check(st, name)
+    return D
+
+
+MAX_K_GROUPS = 256  # groups per fp8_k_grouped_gemm_tn_contiguous call
+
+
+def k_grouped_fp8_gemm_tn_contiguous(A, sa, B, sb, D, ks, accumulate: bool = False, stream=None):
+    """K-grouped TN GEMM (MoE weight gradient): for each group g, whose K rows are
+    [sum(ks[:g]), sum(ks[:g+1])) of A [K, M] and B [K, N] (e4m3 bytes, K-major),
+    D[g] (+)= sum_kb P_kb * sa[kb, m] * sb[kb, n] with sa [K/128, >=M] and sb [K/128, >=N]
+    (one FP32 scale per column per 128-row block). D is float32 [G, M, N] (unit inner
+    stride); accumulate adds into its old values. ks: per-group K lengths, multiples of
+    128 (a list, or a CPU int tensor)."""
+    A, B = _bytes_view(A), _bytes_view(B)
+    dev = D.device
+    ks = [int(k) for k in (ks.tolist() if isinstance(ks, torch.Tensor) else ks)]
+    G = len(ks)
+    _require(dev.type == "cuda" and all(t.device == dev for t in (A, sa, B, sb)), "tensors must share one GPU")
+    _require(A.dim() == 2 and B.dim() == 2 and A.stride(-1) == 1 and B.stride(-1) == 1,
+             "A and B must be 2-D [K, M] / [K, N] with unit inner stride")
+    _require(D.dtype == torch.float32 and D.dim() == 3 and D.shape[0] == G and D.stride(-1) == 1,
+             "D must be float32 [G, M, N] with unit inner stride")
+    _require(sa.dtype == torch.float32 and sb.dtype == torch.float32 and sa.stride(-1) == 1 and sb.stride(-1) == 1,
+             "sa and sb must be float32 with unit inner stride")
+    M, N = D.shape[1], D.shape[2]
+    K = sum(ks)
+    _require(A.shape[0] == K and B.shape[0] == K and A.shape[1] >= M and B.shape[1] >= N,
+             "A must be [sum(ks), >=M] and B [sum(ks), >=N]")
+    _require(sa.shape[0] == K // 128 and sb.shape[0] == K // 128 and sa.shape[1] >= M and sb.shape[1] >= N,
+             "sa must be [K/128, >=M] and sb [K/128, >=N]")
+    ks_arr = (ctypes.c_int32 * max(G, 1))(*ks)
+    st = lib().fp8_k_grouped_gemm_tn_contiguous(
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb), sb.stride(0),
+        _ptr(D), D.stride(1), D.stride(0), ctypes.cast(ks_arr, ctypes.c_void_p), G, M, N, int(bool(accumulate)),
+        _stream(dev, stream))
+    _check(st, "fp8_k_grouped_gemm_tn_contiguous")
     return D
 
 

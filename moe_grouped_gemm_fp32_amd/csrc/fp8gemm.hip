@@ -20,6 +20,7 @@
 #include <mutex>
 
 #include "fp8gemm_kernel.hpp"
+#include "fp8kgroup_kernel.hpp"
 #include "fp8quant_kernel.hpp"
 
 namespace {
@@ -494,6 +495,47 @@ int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t
   else
     hipLaunchKernelGGL(fp8gemm::quantize_1x128_kernel<float>, dim3(grid), dim3(256), 0, stream,
                        static_cast<const float*>(X), ldx, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+
+int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                     int64_t ldb, const float* sb, int64_t ld_sb, float* D, int64_t ldd,
+                                     int64_t d_gstride, const int32_t* ks, int G, int M, int N, int accumulate,
+                                     hipStream_t stream) {
+  if (!A || !sa || !B || !sb || !D || !ks) return FP8GEMM_ERR_NULL;
+  if (G <= 0 || G > fp8gemm::kMaxKGroups || M <= 0 || N <= 0) return FP8GEMM_ERR_SHAPE;
+  fp8gemm::KParams p{};
+  int64_t kb = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] < 0 || ks[g] % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
+    kb += ks[g] / fp8gemm::kBlockK;
+    if (kb * fp8gemm::kBlockK > INT32_MAX) return FP8GEMM_ERR_SHAPE;
+    p.kb_start[g + 1] = (int)kb;
+  }
+  // 16-byte row chunks; 32 rows of either operand addressed with 32-bit lane offsets
+  if (lda < M || lda % 16 != 0 || ldb < N || ldb % 16 != 0 || lda > (1 << 26) || ldb > (1 << 26))
+    return FP8GEMM_ERR_LAYOUT;
+  if (ld_sa < M || ld_sb < N || ldd < N || (G > 1 && d_gstride < (int64_t)(M - 1) * ldd + N))
+    return FP8GEMM_ERR_LAYOUT;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 4))
+    return FP8GEMM_ERR_LAYOUT;
+  int st;
+  effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  p.A = static_cast<const uint8_t*>(A);
+  p.sa = sa;
+  p.B = static_cast<const uint8_t*>(B);
+  p.sb = sb;
+  p.D = D;
+  p.lda = lda, p.ld_sa = ld_sa, p.ldb = ldb, p.ld_sb = ld_sb, p.ldd = ldd, p.d_gstride = d_gstride;
+  p.M = M, p.N = N, p.G = G;
+  p.tiles_m = (int)ceil_div(M, fp8gemm::kg::BM);
+  p.tiles_n = (int)ceil_div(N, fp8gemm::kg::BN);
+  p.accumulate = accumulate ? 1 : 0;
+  p.vec4 = (ldd % 4 == 0 && (G == 1 || d_gstride % 4 == 0) && aligned(D, 16)) ? 1 : 0;
+  const int64_t tiles = (int64_t)G * p.tiles_m * p.tiles_n;
+  if (tiles > INT32_MAX) return FP8GEMM_ERR_SHAPE;
+  hipLaunchKernelGGL(fp8gemm::fp8_k_grouped_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 

@@ -405,3 +405,11 @@ def k_grouped_case(tokens: Sequence[int], M: int, N: int, seed: int, device="cpu
     D = torch.full((len(ks), M, N), float("nan"), dtype=torch.float32, device=device)
     return dict(kind="k_grouped", M=M, N=N, K=K, G=len(ks), ks=ks, tokens=list(tokens),
                 A=A, sa=sa, B=B, sb=sb, lda=lda, ldb=ldb, D=D)
+
+
+def k_grouped_tokens(G: int = 8, seed: int = 0, mean: int = 2048, spread: float = 0.5) -> List[int]:
+    """Tokens routed to each of G local experts: uniform integers in
+    [mean (1 - spread), mean (1 + spread)] (the weight-gradient workload's segment mix)."""
+    gen = make_generator(seed, "cpu")
+    lo, hi = int(mean * (1 - spread)), int(mean * (1 + spread))
+    return torch.randint(lo, hi + 1, (G,), generator=gen).tolist()

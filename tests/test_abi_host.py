@@ -181,3 +181,29 @@ def test_c_argument_validation_without_launch():
     st = L.fp8_gemm_nt_c(P(1 << 20), 512, P(1 << 20), 64, P(1 << 20), 512, P(1 << 20), P(1 << 20), 256,
                          P(1 << 20), 256, 0, 256, 512, None, 0, None)
     assert st == 0                               # M == 0: nothing to do
+
+
+def test_k_grouped_argument_validation_without_launch():
+    L = fg.lib()
+    base = dict(A=1 << 20, lda=4096, sa=1 << 20, ld_sa=4096, B=1 << 20, ldb=7168, sb=1 << 20, ld_sb=7168,
+                D=1 << 20, ldd=7168, d_gstride=4096 * 7168, ks=[256, 128], M=4096, N=7168, acc=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        ks = a["ks"] or []
+        arr = (ctypes.c_int32 * max(len(ks), 1))(*ks)
+        G = kw.get("G", len(ks))
+        return L.fp8_k_grouped_gemm_tn_contiguous(
+            P(a["A"]), a["lda"], P(a["sa"]), a["ld_sa"], P(a["B"]), a["ldb"], P(a["sb"]), a["ld_sb"],
+            P(a["D"]), a["ldd"], a["d_gstride"], ctypes.cast(arr, ctypes.c_void_p) if a["ks"] is not None else None,
+            G, a["M"], a["N"], a["acc"], None)
+
+    assert call(A=0) == -1 and call(sb=0) == -1 and call(D=0) == -1 and call(ks=None, G=2) == -1
+    assert call(ks=[200]) == -2 and call(ks=[-128]) == -2 and call(M=0) == -2 and call(N=0) == -2
+    assert call(G=0) == -2 and call(ks=[128] * 257) == -2
+    assert call(lda=4095) == -3 and call(lda=4104) == -3 and call(ldb=7100) == -3
+    assert call(ld_sa=4000) == -3 and call(ld_sb=7000) == -3 and call(ldd=7000) == -3
+    assert call(d_gstride=4095 * 7168) == -3 and call(A=(1 << 20) + 8) == -3 and call(D=(1 << 20) + 2) == -3
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == -5 and call(ks=[0, 0]) == -5   # valid: stops at the device check
