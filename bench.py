@@ -102,6 +102,33 @@ def pmc_summary(args, shapes):
     print(json.dumps(out))
 
 
+def kg_pmc_summary(args):
+    """HBM traffic of the K-grouped kernel from FETCH_SIZE / WRITE_SIZE runs of
+    --workload kgrouped, scaled by the copy-kernel factors stored in the dense traffic
+    table (measured in the same session); dispatch i belongs to case i mod 2."""
+    fetch_dir, write_dir = args.kg_pmc_summary
+    with open(args.traffic_file) as fh:
+        dense = json.load(fh)
+    ff, fw = dense["fetch_factor"], dense["write_factor"]
+    fetch = [v for k, v in read_counter_csv(fetch_dir, "FETCH_SIZE") if "k_grouped" in k]
+    write = [v for k, v in read_counter_csv(write_dir, "WRITE_SIZE") if "k_grouped" in k]
+    import synth
+    ks = [(t + 127) // 128 * 128 for t in synth.k_grouped_tokens(KGROUP_EXPERTS, seed=9600)]
+    table = {}
+    for i, (M, N) in enumerate(KGROUP_CASES):
+        f, w = fetch[i::len(KGROUP_CASES)], write[i::len(KGROUP_CASES)]
+        fk, wk = sum(f) / len(f), sum(w) / len(w)
+        _, algo = kgrouped_work(M, N, ks)
+        traffic = fk * 1024.0 * ff + wk * 1024.0 * fw
+        table["%d,%d" % (M, N)] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                   "bytes_per_launch": round(traffic), "algo_bytes": algo,
+                                   "traffic_over_algo": round(traffic / algo, 3)}
+    out = {"kernel_sha": kernel_source_hash(), "fetch_factor": ff, "write_factor": fw, "ks": ks, "cases": table}
+    with open(os.path.join(ROOT, "profiles", "traffic_kgrouped.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def trace_summary(d, shapes):
     """Per-shape average GEMM kernel duration from a rocprofv3 --kernel-trace csv directory
     (dispatch i of the GEMM kernel belongs to shape i mod len(shapes))."""
@@ -194,6 +221,18 @@ def parse_shapes(text):
         m, n, k = (int(x) for x in item.split(","))
         out.append((m, n, k))
     return out
+
+
+def blas_threads():
+    """Threads the oracle's matrix products use (numpy's BLAS pool), else the usable cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            return int(blas[0].get("num_threads"))
+    except Exception:  # pragma: no cover
+        pass
+    return len(os.sched_getaffinity(0))
 
 
 def cpu_baseline():
@@ -426,13 +465,129 @@ def quant_bench(args):
     print(json.dumps(out), flush=True)
 
 
+# MoE weight-gradient shapes of the K-grouped TN GEMM: per local expert, dW_gate+up [4096,
+# 7168] = dH^T X and dW_down [7168, 2048] = dY^T H, reduced over that expert's tokens
+KGROUP_CASES = [(4096, 7168), (7168, 2048)]
+KGROUP_EXPERTS = 8
+
+
+def kgrouped_work(M, N, ks, accumulate=False):
+    """Algorithmic FLOPs and HBM bytes of one K-grouped call: every operand byte and scale
+    read once, D written once (and read once when accumulating)."""
+    K = sum(ks)
+    flops = 2.0 * M * N * K
+    nbytes = K * (M + N) + (K // 128) * (M + N) * 4 + len(ks) * M * N * 4 * (2 if accumulate else 1)
+    return flops, nbytes
+
+
+def kgrouped_cpu_baseline(ks, M, N):
+    """The oracle (as it stands) on a bounded sample: M x N outputs of every group."""
+    import numpy as np
+    import oracle
+    import synth
+    c = synth.k_grouped_case([k for k in ks], M, N, seed=98, device="cpu")
+    args = [c[k].numpy() for k in ("A", "sa", "B", "sb")]
+    t0 = time.perf_counter()
+    oracle.k_grouped_tn(*args, c["ks"])
+    dt = time.perf_counter() - t0
+    flops = 2.0 * M * N * sum(c["ks"])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "oracle k_grouped_tn on the same %d expert segments (K=%d) at M=%d, N=%d" % (
+                len(ks), sum(c["ks"]), M, N)}
+
+
+def kgrouped_bench(args):
+    """--workload kgrouped: the K-grouped TN GEMM (MoE weight gradient) on the two expert
+    projections, 8 local experts with 1024..3072 tokens each (K ~ 16.5K), FP32 output.
+    One JSON line; value = FP8 TFLOP/s over both calls."""
+    import torch
+    import moe_grouped_gemm_fp32_amd as fg
+    import synth
+
+    dev = torch.device("cuda:0")
+    tokens = synth.k_grouped_tokens(KGROUP_EXPERTS, seed=9600)
+    cases = []
+    for i, (M, N) in enumerate(KGROUP_CASES):
+        c = synth.k_grouped_case(tokens, M, N, seed=9700 + i, device=dev)
+        D = torch.zeros(len(c["ks"]), M, N, dtype=torch.float32, device=dev)
+        flops, nbytes = kgrouped_work(M, N, c["ks"], args.accumulate)
+        fn = (lambda c=c, D=D: fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["ks"],
+                                                                    accumulate=args.accumulate))
+        cases.append(dict(name="wgrad %dx%d G=%d K=%d" % (M, N, len(c["ks"]), c["K"]), fn=fn, flops=flops,
+                          bytes=nbytes, ks=c["ks"]))
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, c in enumerate(cases):
+            if events is not None:
+                events[i][0].record()
+            c["fn"]()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    step()
+    all_ev = []
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
+        step(ev)
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    per = [0.0] * len(cases)
+    for ev in all_ev:
+        for i, (a, b) in enumerate(ev):
+            per[i] += a.elapsed_time(b)
+    rows, total = [], 0.0
+    for i, c in enumerate(cases):
+        ms = per[i] / args.steps
+        total += c["flops"]
+        tf = c["flops"] / (ms * 1e-3) / 1e12
+        gbs = c["bytes"] / (ms * 1e-3) / 1e9
+        rows.append({"case": c["name"], "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_gbs": round(gbs, 1),
+                     "algo_flops": c["flops"], "algo_bytes": c["bytes"]})
+    dom = max(range(len(cases)), key=lambda i: per[i])
+    r = rows[dom]
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic_kgrouped.json")
+    if os.path.exists(tpath) and not args.accumulate:
+        with open(tpath) as fh:
+            tk = json.load(fh)
+        key = "%d,%d" % KGROUP_CASES[dom]
+        if tk.get("kernel_sha") == kernel_source_hash() and key in tk["cases"]:  # this very kernel only
+            traffic = tk["cases"][key]["bytes_per_launch"]
+    out = {"metric": "K-grouped FP8 GEMM (MoE weight gradient) TFLOP/s, 1xMI355X, % of FP8 dense MFMA peak",
+           "value": round(total / (ms_per_step * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+           "config": {"workload": "K-grouped TN GEMM, 8 experts x 1024..3072 tokens, dW gate+up 4096x7168 and "
+                                  "dW down 7168x2048, FP32 out%s" % (", accumulating" if args.accumulate else ""),
+                      "cases": [c["name"] for c in cases]},
+           "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "frac": r["frac"], "traffic": traffic, "kernel": "fp8_k_grouped_tn_kernel",
+                        "case": r["case"]},
+           "per_case": rows}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = kgrouped_cpu_baseline(cases[0]["ks"], 3072, 3072)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("dense", "ue8m0", "grouped", "quant"), default="dense",
+    ap.add_argument("--workload", choices=("dense", "ue8m0", "grouped", "quant", "kgrouped"), default="dense",
                     help="dense: the 18 DeepSeek-V3-like shapes (default); ue8m0: the same shapes with "
                          "power-of-two (UE8M0) scales through fp8_gemm_nt_ue8m0; grouped: contiguous, masked, "
-                         "MoE; quant: the 1x128 activation quantiser")
+                         "MoE; quant: the 1x128 activation quantiser; kgrouped: the K-grouped TN GEMM "
+                         "(MoE weight gradient)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
@@ -441,6 +596,9 @@ def main():
                     help="dense workload as D = C + A B^T with a BF16 C per shape (fp8_gemm_nt_c)")
     ap.add_argument("--ue8m0", action="store_true",
                     help="with --workload grouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
+    ap.add_argument("--accumulate", action="store_true", help="with --workload kgrouped: D += A^T B")
+    ap.add_argument("--kg-pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="build profiles/traffic_kgrouped.json from rocprofv3 --pmc runs of --workload kgrouped")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
     ap.add_argument("--copy-mb", type=int, default=0, help="only run a plain copy of this many MiB")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", help="per-shape durations from a rocprofv3 trace")
@@ -451,6 +609,9 @@ def main():
 
     if args.pmc_summary:
         pmc_summary(args, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        return
+    if args.kg_pmc_summary:
+        kg_pmc_summary(args)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
@@ -474,6 +635,9 @@ def main():
         return
     if args.workload == "quant":
         quant_bench(args)
+        return
+    if args.workload == "kgrouped":
+        kgrouped_bench(args)
         return
 
     import torch

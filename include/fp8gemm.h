@@ -208,7 +208,7 @@ int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa
  * operands are token-axis activations quantised per column per 128 K rows, and the
  * output is FP32 (weight gradients), optionally accumulated.
  *   A   e4m3 [K][M] (K = sum of ks), row stride lda bytes: lda >= M, lda % 16 == 0,
- *       16-byte aligned, lda <= 2^26. Bytes in columns M..lda-1 are read but unused.
+ *       16-byte aligned, lda <= 2^24. Bytes in columns M..lda-1 are read but unused.
  *   sa  fp32 [K/128][ld_sa]: sa[kb * ld_sa + m], ld_sa >= M, 4-byte aligned.
  *   B   e4m3 [K][N], row stride ldb: as A with N.
  *   sb  fp32 [K/128][ld_sb]: sb[kb * ld_sb + n], ld_sb >= N.

@@ -512,15 +512,15 @@ int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa
     if (kb * fp8gemm::kBlockK > INT32_MAX) return FP8GEMM_ERR_SHAPE;
     p.kb_start[g + 1] = (int)kb;
   }
-  // 16-byte row chunks; 32 rows of either operand addressed with 32-bit lane offsets
-  if (lda < M || lda % 16 != 0 || ldb < N || ldb % 16 != 0 || lda > (1 << 26) || ldb > (1 << 26))
+  // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
+  if (lda < M || lda % 16 != 0 || ldb < N || ldb % 16 != 0 || lda > (1 << 24) || ldb > (1 << 24))
     return FP8GEMM_ERR_LAYOUT;
   if (ld_sa < M || ld_sb < N || ldd < N || (G > 1 && d_gstride < (int64_t)(M - 1) * ldd + N))
     return FP8GEMM_ERR_LAYOUT;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 4))
     return FP8GEMM_ERR_LAYOUT;
   int st;
-  effective_cus(true, &st);
+  const int cus = effective_cus(true, &st);
   if (st != FP8GEMM_OK) return st;
   p.A = static_cast<const uint8_t*>(A);
   p.sa = sa;
@@ -529,13 +529,22 @@ int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa
   p.D = D;
   p.lda = lda, p.ld_sa = ld_sa, p.ldb = ldb, p.ld_sb = ld_sb, p.ldd = ldd, p.d_gstride = d_gstride;
   p.M = M, p.N = N, p.G = G;
-  p.tiles_m = (int)ceil_div(M, fp8gemm::kg::BM);
-  p.tiles_n = (int)ceil_div(N, fp8gemm::kg::BN);
   p.accumulate = accumulate ? 1 : 0;
   p.vec4 = (ldd % 4 == 0 && (G == 1 || d_gstride % 4 == 0) && aligned(D, 16)) ? 1 : 0;
+  // 256x256 tiles (8 waves of 64x128) once they alone give every CU a tile; else 128x128
+  // (4 waves of 64x64, two workgroups per CU). Both use a 2-stage ring: a 3-stage 256x128
+  // instance (64x64 per wave) measured slower than the 256x256 one on the weight-gradient
+  // shapes, whose per-flop LDS reads are 25% lower.
+  const bool big = (int64_t)G * ceil_div(M, 256) * ceil_div(N, 256) >= cus;
+  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
+  p.tiles_m = (int)ceil_div(M, bm);
+  p.tiles_n = (int)ceil_div(N, bn);
   const int64_t tiles = (int64_t)G * p.tiles_m * p.tiles_n;
   if (tiles > INT32_MAX) return FP8GEMM_ERR_SHAPE;
-  hipLaunchKernelGGL(fp8gemm::fp8_k_grouped_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  if (big)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2>), dim3((unsigned)tiles), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 

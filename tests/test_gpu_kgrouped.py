@@ -20,6 +20,15 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["128x128", "256x256"])
+def tile(request):
+    """Select the tile instance through the CU count the planner sees: the 256x256 tiles
+    are taken once they alone give every CU a tile."""
+    fg.set_num_cus(1 if request.param == "256x256" else 1 << 20)
+    yield request.param
+    fg.set_num_cus(0)
+
+
 def _host(c):
     """The oracle's operands: A [K, M] and B [K, N] without the padding columns."""
     return [c["A"][:, :c["M"]].cpu().numpy(), c["sa"].cpu().numpy(),
@@ -67,20 +76,21 @@ CASES = [
     ([200, 57], 200, 136, 208, 144),          # ragged M / N tails, padded rows
     ([129], 40, 24, 48, 32),                  # one partial tile
     ([1000, 640, 0, 30], 128, 640, None, None),
+    ([300, 500], 520, 600, 528, 608),          # three 256-row tile rows, ragged last ones
 ]
 
 
 @pytest.mark.parametrize("kind", ["normal", "e1"])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_parity(cuda_device, kind, case):
+def test_parity(cuda_device, tile, kind, case):
     tokens, M, N, lda, ldb = CASES[case]
     c = synth.k_grouped_case(tokens, M, N, seed=9100 + case, device=cuda_device, kind=kind, lda=lda, ldb=ldb)
     got = run(c)
-    check(c, got, exact=kind == "e1", what=f"{kind} case {case}")
+    check(c, got, exact=kind == "e1", what=f"{tile} {kind} case {case}")
 
 
 @pytest.mark.parametrize("kind", ["normal", "e1"])
-def test_accumulate(cuda_device, kind):
+def test_accumulate(cuda_device, tile, kind):
     c = synth.k_grouped_case([256, 0, 128], 192, 160, seed=9200, device=cuda_device, kind=kind)
     gen = synth.make_generator(9201, cuda_device)
     D0 = torch.randint(-64, 65, (3, 192, 160), generator=gen, device=cuda_device).float() / 4
@@ -93,7 +103,7 @@ def test_accumulate(cuda_device, kind):
     assert torch.all(run(c)[1] == 0)
 
 
-def test_strided_and_misaligned_d(cuda_device):
+def test_strided_and_misaligned_d(cuda_device, tile):
     c = synth.k_grouped_case([384, 128], 136, 100, seed=9300, device=cuda_device, kind="e1", lda=144, ldb=112)
     big = torch.full((2 * 150 * 103 + 1,), float("nan"), device=cuda_device)
     D = big[1:].view(2, 150, 103)[:, :136, :100]          # ldd 103 (odd), 4-byte aligned only
