@@ -576,7 +576,7 @@ def kgrouped_bench(args):
                         "case": r["case"]},
            "per_case": rows}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = kgrouped_cpu_baseline(cases[0]["ks"], 3072, 3072)
+        out["cpu_baseline"] = kgrouped_cpu_baseline(cases[0]["ks"], 5120, 5120)
     print(json.dumps(out), flush=True)
 
 
