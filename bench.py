@@ -499,8 +499,9 @@ def kgrouped_cpu_baseline(ks, M, N):
 
 def kgrouped_bench(args):
     """--workload kgrouped: the K-grouped TN GEMM (MoE weight gradient) on the two expert
-    projections, 8 local experts with 1024..3072 tokens each (K ~ 16.5K), FP32 output.
-    One JSON line; value = FP8 TFLOP/s over both calls."""
+    projections, 8 local experts with 1024..3072 tokens each (K ~ 16.5K), FP32 output
+    (--ue8m0: power-of-two scales through the UE8M0 call). One JSON line; value = FP8
+    TFLOP/s over both calls."""
     import torch
     import moe_grouped_gemm_fp32_amd as fg
     import synth
@@ -509,11 +510,11 @@ def kgrouped_bench(args):
     tokens = synth.k_grouped_tokens(KGROUP_EXPERTS, seed=9600)
     cases = []
     for i, (M, N) in enumerate(KGROUP_CASES):
-        c = synth.k_grouped_case(tokens, M, N, seed=9700 + i, device=dev)
+        c = synth.k_grouped_case(tokens, M, N, seed=9700 + i, device=dev, kind="pow2" if args.ue8m0 else "normal")
         D = torch.zeros(len(c["ks"]), M, N, dtype=torch.float32, device=dev)
         flops, nbytes = kgrouped_work(M, N, c["ks"], args.accumulate)
         fn = (lambda c=c, D=D: fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["ks"],
-                                                                    accumulate=args.accumulate))
+                                                                    accumulate=args.accumulate, ue8m0=args.ue8m0))
         cases.append(dict(name="wgrad %dx%d G=%d K=%d" % (M, N, len(c["ks"]), c["K"]), fn=fn, flops=flops,
                           bytes=nbytes, ks=c["ks"]))
     torch.cuda.synchronize()
@@ -558,7 +559,7 @@ def kgrouped_bench(args):
     r = rows[dom]
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic_kgrouped.json")
-    if os.path.exists(tpath) and not args.accumulate:
+    if os.path.exists(tpath) and not args.accumulate and not args.ue8m0:
         with open(tpath) as fh:
             tk = json.load(fh)
         key = "%d,%d" % KGROUP_CASES[dom]
@@ -569,7 +570,8 @@ def kgrouped_bench(args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
            "config": {"workload": "K-grouped TN GEMM, 8 experts x 1024..3072 tokens, dW gate+up 4096x7168 and "
-                                  "dW down 7168x2048, FP32 out%s" % (", accumulating" if args.accumulate else ""),
+                                  "dW down 7168x2048, FP32 out%s%s" % (", accumulating" if args.accumulate else "",
+                                                            ", UE8M0 scales" if args.ue8m0 else ""),
                       "cases": [c["name"] for c in cases]},
            "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                         "frac": r["frac"], "traffic": traffic, "kernel": "fp8_k_grouped_tn_kernel",
@@ -595,7 +597,7 @@ def main():
     ap.add_argument("--with-c", action="store_true",
                     help="dense workload as D = C + A B^T with a BF16 C per shape (fp8_gemm_nt_c)")
     ap.add_argument("--ue8m0", action="store_true",
-                    help="with --workload grouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
+                    help="with --workload grouped or kgrouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--accumulate", action="store_true", help="with --workload kgrouped: D += A^T B")
     ap.add_argument("--kg-pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="build profiles/traffic_kgrouped.json from rocprofv3 --pmc runs of --workload kgrouped")

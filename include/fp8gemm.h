@@ -231,6 +231,20 @@ int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa
                                      hipStream_t stream);
 
 /*
+ * The K-grouped TN GEMM with UE8M0 scale factors: the same operation, layouts,
+ * preconditions and errors as fp8_k_grouped_gemm_tn_contiguous, with every sa and sb
+ * value an exact power of two 2^(e-127), 1 <= e <= 254, held as FP32 (see
+ * fp8_gemm_nt_ue8m0). gfx950's block-scaled MFMA applies them: each lane passes the
+ * exponent of its A row and of its B row, which is the per-column scaling of both
+ * operands, and accumulates the scaled block products itself.
+ */
+int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                           const void* B, int64_t ldb, const float* sb, int64_t ld_sb,
+                                           float* D, int64_t ldd, int64_t d_gstride,
+                                           const int32_t* ks, int G, int M, int N, int accumulate,
+                                           hipStream_t stream);
+
+/*
  * 1x128 activation quantisation: the step upstream of every call above, producing
  * the A operand and its scales (one FP32 scale per row per 128-wide K block:
  * GeekNews topic 19444, intro). The pages leave FP8 conversion to the user

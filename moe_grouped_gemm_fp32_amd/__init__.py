@@ -68,6 +68,8 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_k_grouped_gemm_tn_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
+    "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
@@ -304,13 +306,14 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
 MAX_K_GROUPS = 256  # groups per fp8_k_grouped_gemm_tn_contiguous call
 
 
-def k_grouped_fp8_gemm_tn_contiguous(A, sa, B, sb, D, ks, accumulate: bool = False, stream=None):
+def k_grouped_fp8_gemm_tn_contiguous(A, sa, B, sb, D, ks, accumulate: bool = False, stream=None, ue8m0=False):
     """K-grouped TN GEMM (MoE weight gradient): for each group g, whose K rows are
     [sum(ks[:g]), sum(ks[:g+1])) of A [K, M] and B [K, N] (e4m3 bytes, K-major),
     D[g] (+)= sum_kb P_kb * sa[kb, m] * sb[kb, n] with sa [K/128, >=M] and sb [K/128, >=N]
     (one FP32 scale per column per 128-row block). D is float32 [G, M, N] (unit inner
     stride); accumulate adds into its old values. ks: per-group K lengths, multiples of
-    128 (a list, or a CPU int tensor)."""
+    128 (a list, or a CPU int tensor). ue8m0: every scale is an exact power of two (UE8M0
+    values held as FP32), applied by the block-scaled MFMA."""
     A, B = _bytes_view(A), _bytes_view(B)
     dev = D.device
     ks = [int(k) for k in (ks.tolist() if isinstance(ks, torch.Tensor) else ks)]
@@ -329,11 +332,12 @@ def k_grouped_fp8_gemm_tn_contiguous(A, sa, B, sb, D, ks, accumulate: bool = Fal
     _require(sa.shape[0] == K // 128 and sb.shape[0] == K // 128 and sa.shape[1] >= M and sb.shape[1] >= N,
              "sa must be [K/128, >=M] and sb [K/128, >=N]")
     ks_arr = (ctypes.c_int32 * max(G, 1))(*ks)
-    st = lib().fp8_k_grouped_gemm_tn_contiguous(
+    name = "fp8_k_grouped_gemm_tn_contiguous_ue8m0" if ue8m0 else "fp8_k_grouped_gemm_tn_contiguous"
+    st = getattr(lib(), name)(
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb), sb.stride(0),
         _ptr(D), D.stride(1), D.stride(0), ctypes.cast(ks_arr, ctypes.c_void_p), G, M, N, int(bool(accumulate)),
         _stream(dev, stream))
-    _check(st, "fp8_k_grouped_gemm_tn_contiguous")
+    _check(st, name)
     return D
 
 

@@ -498,10 +498,12 @@ int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 
-int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
-                                     int64_t ldb, const float* sb, int64_t ld_sb, float* D, int64_t ldd,
-                                     int64_t d_gstride, const int32_t* ks, int G, int M, int N, int accumulate,
-                                     hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+int k_grouped_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                 const float* sb, int64_t ld_sb, float* D, int64_t ldd, int64_t d_gstride, const int32_t* ks, int G,
+                 int M, int N, int accumulate, hipStream_t stream, bool e8) {
   if (!A || !sa || !B || !sb || !D || !ks) return FP8GEMM_ERR_NULL;
   if (G <= 0 || G > fp8gemm::kMaxKGroups || M <= 0 || N <= 0) return FP8GEMM_ERR_SHAPE;
   fp8gemm::KParams p{};
@@ -541,11 +543,36 @@ int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa
   p.tiles_n = (int)ceil_div(N, bn);
   const int64_t tiles = (int64_t)G * p.tiles_m * p.tiles_n;
   if (tiles > INT32_MAX) return FP8GEMM_ERR_SHAPE;
-  if (big)
+  if (big && e8)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, true>), dim3((unsigned)tiles), dim3(512), 0,
+                       stream, p);
+  else if (big)
     hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2>), dim3((unsigned)tiles), dim3(512), 0, stream, p);
+  else if (e8)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, true>), dim3((unsigned)tiles), dim3(256), 0,
+                       stream, p);
   else
     hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" {
+
+int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
+                                     int64_t ldb, const float* sb, int64_t ld_sb, float* D, int64_t ldd,
+                                     int64_t d_gstride, const int32_t* ks, int G, int M, int N, int accumulate,
+                                     hipStream_t stream) {
+  return k_grouped_tn(A, lda, sa, ld_sa, B, ldb, sb, ld_sb, D, ldd, d_gstride, ks, G, M, N, accumulate, stream,
+                      false);
+}
+
+int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                           const void* B, int64_t ldb, const float* sb, int64_t ld_sb, float* D,
+                                           int64_t ldd, int64_t d_gstride, const int32_t* ks, int G, int M, int N,
+                                           int accumulate, hipStream_t stream) {
+  return k_grouped_tn(A, lda, sa, ld_sa, B, ldb, sb, ld_sb, D, ldd, d_gstride, ks, G, M, N, accumulate, stream,
+                      true);
 }
 
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m) {

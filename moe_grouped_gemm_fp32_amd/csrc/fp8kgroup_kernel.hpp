@@ -67,7 +67,12 @@ struct Layout {
 __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >> 3) & 4); }
 }  // namespace kg
 
-template <int WAVES_M, int WAVES_N, int TNW, int STAGES>
+// E8 instances take power-of-two scales (UE8M0 values 2^(e-127) held as FP32): the
+// block-scaled MFMA multiplies each 128-K block product by 2^(ea[m]-127) * 2^(eb[n]-127)
+// -- one exponent per lane for its A row and one for its B row, which is exactly the
+// per-column scaling of both operands -- and accumulates it itself, so no promotion
+// VALU work is left.
+template <int WAVES_M, int WAVES_N, int TNW, int STAGES, bool E8 = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_kernel(const KParams p) {
   using namespace kg;
   constexpr int NW = WAVES_M * WAVES_N;
@@ -174,6 +179,30 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     for (int t = 0; t < 4; ++t) {
       fa[t] = read_frag(st + frag_off(4 * wm + t));
       sa_t[t] = s_a[64 * wm + 16 * t + li];
+    }
+    if constexpr (E8) {
+      // operand scales: lane l carries the exponent of its A row 16 t + l % 16 and of its
+      // B row 16 j + l % 16 (the same for its four 32-K chunks: one block scale)
+      int ea[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ea[t] = (__float_as_int(sa_t[t]) >> 23) & 0xFF;
+#pragma unroll
+      for (int jh = 0; jh < TNW / 4; ++jh) {
+        v8i fb[4];
+        int eb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fb[j] = read_frag(st + LY::b_off + frag_off(TNW * wn + 4 * jh + j));
+          eb[j] = (__float_as_int(s_b[16 * (TNW * wn + 4 * jh + j) + li]) >> 23) & 0xFF;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[t][4 * jh + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fb[j], fa[t], acc[t][4 * jh + j], 0, 0, 0, eb[j], 0, ea[t]);
+      }
+      continue;
     }
 #pragma unroll
     for (int jh = 0; jh < TNW / 4; ++jh) {

@@ -143,3 +143,43 @@ def test_full_size_sampled(cuda_device, M, N):
     rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 12, replace=False)]))
     cols = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.choice(N, 12, replace=False)]))
     check(c, got, rows=rows, cols=cols, what=f"full {M}x{N}")
+
+
+# ---- UE8M0 (power-of-two) scales through fp8_k_grouped_gemm_tn_contiguous_ue8m0: the
+# oracle is the same K-grouped definition on the same power-of-two FP32 scale values
+@pytest.mark.parametrize("kind", ["pow2", "e1"])
+@pytest.mark.parametrize("case", [1, 2, 4, 5])
+def test_ue8m0_parity(cuda_device, tile, kind, case):
+    tokens, M, N, lda, ldb = CASES[case]
+    c = synth.k_grouped_case(tokens, M, N, seed=9800 + case, device=cuda_device, kind=kind, lda=lda, ldb=ldb)
+    D = c["D"].clone()
+    fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["ks"], ue8m0=True)
+    torch.cuda.synchronize()
+    check(c, D, exact=kind == "e1", what=f"ue8m0 {tile} {kind} case {case}")
+
+
+def test_ue8m0_accumulate_matches_fp32_scale_path(cuda_device):
+    c = synth.k_grouped_case([300, 0, 500], 256, 384, seed=9900, device=cuda_device, kind="pow2")
+    gen = synth.make_generator(9901, cuda_device)
+    D0 = torch.randn(3, 256, 384, generator=gen, device=cuda_device)
+    a, b = D0.clone(), D0.clone()
+    fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], a, c["ks"], accumulate=True, ue8m0=True)
+    fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], b, c["ks"], accumulate=True)
+    torch.cuda.synchronize()
+    check(c, a, D_in=D0.cpu().numpy(), what="ue8m0 accumulate")
+    assert torch.equal(a[1], D0[1])
+    rel = float(((a - b) ** 2).sum() / (b ** 2).sum())
+    assert rel < 1e-9, f"UE8M0 and FP32-scale paths differ: {rel:.3e}"
+
+
+@pytest.mark.parametrize("M,N", [(4096, 7168)])
+def test_ue8m0_full_size_sampled(cuda_device, M, N):
+    tokens = synth.k_grouped_tokens(8, seed=9600)
+    c = synth.k_grouped_case(tokens, M, N, seed=9602, device=cuda_device, kind="pow2")
+    D = c["D"].clone()
+    fg.k_grouped_fp8_gemm_tn_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["ks"], ue8m0=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + 1)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, 12, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.choice(N, 12, replace=False)]))
+    check(c, D, rows=rows, cols=cols, what=f"ue8m0 full {M}x{N}")
