@@ -333,3 +333,28 @@ def k_grouped_tn_abs(A, sa, B, sb, ks, rows=None, cols=None):
 
 # code of |value| for every e4m3 code (sign bit cleared; NaN codes kept)
 E4M3_TABLE_ABS_CODES = (np.arange(256) & 0x7F).astype(np.uint8)
+
+
+# ------------------------------------------------------------ SwiGLU + 1x128 quantisation
+# The MoE FFN's step between its two GEMMs is SwiGLU (es.news.hada.io/topic?id=19459,
+# "Mega MoE": linear 1, SwiGLU, linear 2); its output is the down projection's A operand,
+# quantised 1x128 as above. Reading: the gate+up output row holds gate in its first F
+# columns and up in the last F; silu(g) = g * sigmoid(g) = g / (1 + e^-g); padding rows of
+# the contiguous layout (m_indices = -1) are zeros.
+def swiglu(h: np.ndarray) -> np.ndarray:
+    """h [R, 2F] (float32 values) -> the SwiGLU value silu(gate) * up in FP64."""
+    h = np.asarray(h, dtype=np.float32).astype(np.float64)
+    F = h.shape[1] // 2
+    g, u = h[:, :F], h[:, F:]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def swiglu_quantize_1x128(h: np.ndarray, m_indices=None):
+    """(codes uint8 [R, F], scales float32 [F/128, R], y float32 [R, F]): the SwiGLU value
+    rounded once to FP32, padding rows zeroed, then quantize_1x128."""
+    y = swiglu(h).astype(np.float32)
+    if m_indices is not None:
+        y[np.asarray(m_indices)[:y.shape[0]] < 0] = 0.0
+    q, s = quantize_1x128(y)
+    return q, s, y
