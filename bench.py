@@ -394,14 +394,16 @@ def grouped_bench(args):
 
 
 QUANT_CASES = [(4096, 7168, "bf16"), (4096, 2048, "bf16"), (4096, 16384, "bf16"), (32768, 7168, "bf16"),
-               (53376, 2048, "bf16"), (4096, 7168, "fp32")]
+               (53376, 2048, "bf16"), (4096, 7168, "fp32"), (53376, 2048, "swiglu-bf16")]
 
 
 def quant_bench(args):
     """--workload quant: the 1x128 activation quantiser on the activation shapes that feed
     the GEMMs (dense M=4096 at K = 7168, 2048, 16384; the MoE gate+up input of 32768
     routed rows at K=7168; the MoE down input of 53376 padded rows at K=2048; one FP32
-    input). HBM-bound: bytes = input once + e4m3 codes + FP32 scales. One JSON line."""
+    input; and SwiGLU fused with the quantisation on the MoE down input, reading the
+    53376 x 4096 BF16 gate+up output). HBM-bound: bytes = input once + e4m3 codes + FP32
+    scales. One JSON line."""
     import torch
     import moe_grouped_gemm_fp32_amd as fg
 
@@ -410,14 +412,18 @@ def quant_bench(args):
     for i, (M, K, dt) in enumerate(QUANT_CASES):
         g = torch.Generator(device=dev)
         g.manual_seed(7000 + i)
-        X = torch.randn(M, K, generator=g, device=dev, dtype=torch.float32)
-        if dt == "bf16":
+        swiglu = dt.startswith("swiglu")
+        X = torch.randn(M, 2 * K if swiglu else K, generator=g, device=dev, dtype=torch.float32)
+        if dt.endswith("bf16"):
             X = X.to(torch.bfloat16)
         Q = torch.empty(M, K, dtype=torch.uint8, device=dev)
         sa = torch.empty(K // 128, fg.scale_ld(M), dtype=torch.float32, device=dev)
-        nbytes = M * K * X.element_size() + M * K + M * (K // 128) * 4
-        cases.append(dict(name="%s %dx%d" % (dt, M, K), fn=(lambda X=X, Q=Q, sa=sa: fg.quantize_1x128(X, Q, sa)),
-                          bytes=nbytes))
+        nbytes = X.numel() * X.element_size() + M * K + M * (K // 128) * 4
+        if swiglu:
+            fn = lambda X=X, Q=Q, sa=sa: fg.swiglu_quantize_1x128(X, None, Q, sa)
+        else:
+            fn = lambda X=X, Q=Q, sa=sa: fg.quantize_1x128(X, Q, sa)
+        cases.append(dict(name="%s %dx%d" % (dt, M, K), fn=fn, bytes=nbytes))
     torch.cuda.synchronize()
 
     def step(events=None):

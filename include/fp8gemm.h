@@ -267,6 +267,28 @@ enum { FP8GEMM_QUANT_BF16 = 0, FP8GEMM_QUANT_FP32 = 1 };
 int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t ldq,
                        float* sa, int64_t ld_sa, int M, int K, hipStream_t stream);
 
+/*
+ * The same quantisation fused with the SwiGLU of the MoE FFN, producing the down
+ * projection's A operand from the gate+up projection's output: the MoE pipeline the
+ * pages list runs linear 1, then SwiGLU, then linear 2 (es.news.hada.io/topic?id=19459,
+ * "Mega MoE"), and the grouped calls compute the two linears. The SwiGLU reading (gate
+ * half first, silu(x) = x * sigmoid(x)) is the standard one; the pages give no formula.
+ * Per row r and column k < F, in FP32:
+ *     y = silu(g) * u,  silu(g) = g / (1 + exp(-g)),  g = H[r][k], u = H[r][F + k]
+ * then y is quantised exactly as by fp8_quantize_1x128 (s = amax / 448 per 128-column
+ * block, q = e4m3_rne(y / s)). exp is the device's FP32 exponential (within a few
+ * units in the last place), the division correctly rounded.
+ *   H  [M, 2F] row-major (gate in columns 0..F-1, up in F..2F-1), row stride ldh
+ *      (elements) >= 2F, BF16 or FP32 (h_dtype); 16-byte aligned, ldh a multiple
+ *      of 8 (BF16) or 4 (FP32); F a positive multiple of 128.
+ *   m_indices  optional int32 [M] (NULL: every row live): rows with -1 (padding of
+ *      the contiguous layout) quantise as zeros (codes 0, scale 1).
+ *   Q, sa  as for fp8_quantize_1x128 with K = F.
+ * Errors as for fp8_quantize_1x128 (_SHAPE for F <= 0 or F % 128).
+ */
+int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,
+                              int64_t ldq, float* sa, int64_t ld_sa, int M, int F, hipStream_t stream);
+
 /* Bytes of split-K workspace the call with these sizes may use (0 = never splits).
  * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked). */
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m);

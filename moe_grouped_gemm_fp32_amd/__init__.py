@@ -72,6 +72,7 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
+    "fp8_swiglu_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
     "fp8_gemm_force_config": (_INT, [ctypes.POINTER(Config)]),
     "fp8_gemm_set_num_cus": (_INT, [_INT]),
@@ -227,6 +228,35 @@ def quantize_1x128(X: torch.Tensor, Q: Optional[torch.Tensor] = None, sa: Option
     st = lib().fp8_quantize_1x128(_ptr(X), X.stride(0), QUANT_BF16 if X.dtype == torch.bfloat16 else QUANT_FP32,
                                   _ptr(Q), Q.stride(0), _ptr(sa), sa.stride(0), M, K, _stream(X.device, stream))
     _check(st, "fp8_quantize_1x128")
+    return Q, sa
+
+
+def swiglu_quantize_1x128(H: torch.Tensor, m_indices: Optional[torch.Tensor] = None, Q: Optional[torch.Tensor] = None,
+                          sa: Optional[torch.Tensor] = None, stream=None):
+    """SwiGLU of a gate+up output fused with the 1x128 quantisation: H [M, 2F] (bfloat16 or
+    float32, gate in the first F columns) -> (Q e4m3 bytes [M, F], sa float32 [F/128,
+    ld_sa]) of y = silu(gate) * up, computed by fp8_swiglu_quantize_1x128; rows whose
+    m_indices entry is -1 quantise as zeros."""
+    _require(H.device.type == "cuda" and H.dim() == 2 and H.stride(-1) == 1, "H must be a 2-D GPU tensor")
+    _require(H.dtype in (torch.bfloat16, torch.float32), "H must be bfloat16 or float32")
+    M, F2 = H.shape
+    F = F2 // 2
+    _require(F2 % 2 == 0 and F % 128 == 0, "H must be [M, 2F] with F a multiple of 128")
+    if Q is None:
+        Q = torch.empty(M, F, dtype=torch.uint8, device=H.device)
+    if sa is None:
+        sa = torch.empty(F // 128, scale_ld(M), dtype=torch.float32, device=H.device)
+    Q = _bytes_view(Q)
+    _require(tuple(Q.shape) == (M, F) and Q.stride(-1) == 1 and Q.device == H.device, "Q must be [M, F]")
+    _require(sa.dtype == torch.float32 and sa.shape[0] == F // 128 and sa.stride(-1) == 1 and sa.stride(0) >= M,
+             "sa must be float32 [F/128, >=M]")
+    if m_indices is not None:
+        _require(m_indices.dtype == torch.int32 and m_indices.numel() >= M and m_indices.device == H.device,
+                 "m_indices must be int32 [>=M] on H's device")
+    st = lib().fp8_swiglu_quantize_1x128(_ptr(H), H.stride(0), QUANT_BF16 if H.dtype == torch.bfloat16 else QUANT_FP32,
+                                         _ptr(m_indices), _ptr(Q), Q.stride(0), _ptr(sa), sa.stride(0), M, F,
+                                         _stream(H.device, stream))
+    _check(st, "fp8_swiglu_quantize_1x128")
     return Q, sa
 
 

@@ -575,6 +575,33 @@ int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const flo
                       true);
 }
 
+int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,
+                              int64_t ldq, float* sa, int64_t ld_sa, int M, int F, hipStream_t stream) {
+  if (!H || !Q || !sa) return FP8GEMM_ERR_NULL;
+  if (M < 0 || F <= 0 || F % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
+  if (h_dtype != FP8GEMM_QUANT_BF16 && h_dtype != FP8GEMM_QUANT_FP32) return FP8GEMM_ERR_LAYOUT;
+  const int64_t h_align = h_dtype == FP8GEMM_QUANT_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (ldh < 2 * (int64_t)F || ldh % h_align != 0 || ldq < F || ldq % 8 != 0 || ld_sa < M || ld_sa % 4 != 0)
+    return FP8GEMM_ERR_LAYOUT;
+  if (!aligned(H, 16) || !aligned(Q, 8) || !aligned(sa, 4) || !aligned(m_indices, 4)) return FP8GEMM_ERR_LAYOUT;
+  int st;
+  const int cus = effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  const int nkb = F / fp8gemm::kBlockK;
+  const int64_t items = ceil_div(M, 4) * nkb;  // one wave each
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 4), (int64_t)cus * 8));
+  if (h_dtype == FP8GEMM_QUANT_BF16)
+    hipLaunchKernelGGL((fp8gemm::quantize_1x128_kernel<uint16_t, true>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(H), ldh, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb,
+                       m_indices, F);
+  else
+    hipLaunchKernelGGL((fp8gemm::quantize_1x128_kernel<float, true>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const float*>(H), ldh, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb,
+                       m_indices, F);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 || kind == FP8GEMM_KIND_MASKED) return 0;
   int st;

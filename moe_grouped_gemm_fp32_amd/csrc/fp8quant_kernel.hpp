@@ -39,9 +39,14 @@ __device__ __forceinline__ void load8(const T* src, float (&x)[8]) {
   }
 }
 
-template <typename T>
+// SWIGLU instances quantise y = silu(gate) * up of a row [gate (F) | up (F)] (the MoE
+// down projection's input): gate at column k, up at column F + k, in FP32 with
+// silu(g) = g / (1 + exp(-g)) (the division correctly rounded); rows whose m_indices
+// entry is -1 (contiguous-layout padding) quantise as zeros.
+template <typename T, bool SWIGLU = false>
 __global__ void __launch_bounds__(256) quantize_1x128_kernel(const T* X, int64_t ldx, uint8_t* Q, int64_t ldq,
-                                                             float* sa, int64_t ld_sa, int M, int nkb) {
+                                                             float* sa, int64_t ld_sa, int M, int nkb,
+                                                             const int32_t* m_indices = nullptr, int F = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;  // row within the wave's four
@@ -53,7 +58,18 @@ __global__ void __launch_bounds__(256) quantize_1x128_kernel(const T* X, int64_t
     const int r = rg * 4 + g;
     const bool live = r < M;
     float x[8];
-    if (live) {
+    if constexpr (SWIGLU) {
+      if (live && !(m_indices && m_indices[r] < 0)) {
+        float u[8];
+        load8(X + (int64_t)r * ldx + kb * 128 + c * 8, x);
+        load8(X + (int64_t)r * ldx + F + kb * 128 + c * 8, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = x[i] / (1.0f + expf(-x[i])) * u[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+      }
+    } else if (live) {
       load8(X + (int64_t)r * ldx + kb * 128 + c * 8, x);
     } else {
 #pragma unroll

@@ -1,0 +1,107 @@
+"""GPU parity of the SwiGLU-fused 1x128 quantisation (fp8_swiglu_quantize_1x128 through
+the C ABI) against the CPU oracle (oracle.swiglu_quantize_1x128).
+
+The kernel evaluates silu with the device's FP32 exponential, which is within a few
+units in the last place of the exact value, so its y can differ from the oracle's
+correctly rounded FP32 y by a few ulp; both then take every quantisation decision in
+FP32. The bar: every scale within 2^-20 relative of the oracle's; every code equal to
+the oracle's, except where the oracle's quotient y/s lies within 2^-18 (relative) of a
+rounding midpoint, where the code must be one of the two codes beside it; and, for every
+element, the dequantised GPU value within half an e4m3 step (times the scale, plus 2^-18
+relative) of the exact SwiGLU value -- the quantiser's own error bound. Padding rows
+(m_indices = -1) must be zero codes with unit scales, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_fp32_amd as fg
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+POS = oracle.E4M3_TABLE[:0x7F]                      # increasing values of codes 0x00..0x7E
+
+
+def _step(a):
+    """e4m3 spacing at magnitude a (the gap to the next code above)."""
+    hi = np.clip(np.searchsorted(POS, a, side="right"), 1, 0x7E)
+    return POS[hi] - POS[hi - 1]
+
+
+def _check(H, mi, what):
+    dev = H.device
+    Q, sa = fg.swiglu_quantize_1x128(H, mi)
+    torch.cuda.synchronize()
+    h = H.float().cpu().numpy()
+    m = None if mi is None else mi.cpu().numpy()
+    q_ref, s_ref, y_ref = oracle.swiglu_quantize_1x128(h, m)
+    M, F = y_ref.shape
+    q, s = Q.cpu().numpy(), sa.cpu().numpy()[:, :M]
+    assert np.all(np.abs(s.astype(np.float64) / s_ref - 1.0) <= 2.0 ** -20), f"{what}: scales"
+    bad = q != q_ref
+    if bad.any():
+        sfull = np.repeat(s_ref.T.astype(np.float64), 128, axis=1)
+        quo = np.abs(y_ref.astype(np.float64)) / sfull
+        r, c = np.nonzero(bad)
+        a = np.minimum(quo[r, c], 448.0)
+        lo_i = np.clip(np.searchsorted(POS, a, side="right") - 1, 0, 0x7D)
+        mid = (POS[lo_i] + POS[lo_i + 1]) / 2
+        near = np.abs(a - mid) <= 2.0 ** -18 * np.maximum(a, POS[1])
+        codes = {int(x) for x in lo_i}
+        assert np.all(near), f"{what}: {int((~near).sum())} code mismatches away from a rounding midpoint"
+        gq = q[r, c] & 0x7F
+        assert np.all((gq == lo_i) | (gq == lo_i + 1)), f"{what}: a mismatched code is not beside the midpoint"
+        assert bad.mean() < 1e-3, f"{what}: {bad.mean():.2e} of the codes differ"
+    # the quantiser's error bound against the exact SwiGLU value
+    exact = oracle.swiglu(h)
+    if m is not None:
+        exact[m[:M] < 0] = 0.0
+    sg = np.repeat(s.T.astype(np.float64), 128, axis=1)
+    deq = oracle.decode_e4m3(q) * sg
+    bound = 0.5 * _step(np.minimum(np.abs(exact) / sg, 448.0)) * sg * (1 + 2.0 ** -18) + 2.0 ** -18 * np.abs(exact)
+    assert np.all(np.abs(deq - exact) <= bound), f"{what}: dequantised values exceed the quantiser's bound"
+    if m is not None:
+        pad = m[:M] < 0
+        assert np.all(q[pad] == 0) and np.all(s[:, pad] == 1.0), f"{what}: padding rows"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,F", [(1, 128), (37, 256), (300, 2048)])
+def test_parity(cuda_device, dtype, M, F):
+    g = synth.make_generator(1200 + M + F, cuda_device)
+    H = (torch.randn(M, 2 * F, generator=g, device=cuda_device) * 2).to(dtype)
+    _check(H, None, f"{dtype} {M}x{F}")
+
+
+def test_contiguous_padding_rows(cuda_device):
+    mi, _ = synth.contiguous_layout([100, 0, 57, 128])
+    M = mi.numel()
+    g = synth.make_generator(1300, cuda_device)
+    H = torch.randn(M, 2 * 512, generator=g, device=cuda_device).to(torch.bfloat16)
+    _check(H, mi.to(cuda_device), "contiguous padding")
+
+
+def test_strided_input_and_wide_range(cuda_device):
+    g = synth.make_generator(1400, cuda_device)
+    big = torch.randn(64, 2 * 384 + 16, generator=g, device=cuda_device)
+    big[:, :384] *= torch.exp2(torch.randint(-20, 20, (64, 1), generator=g, device=cuda_device).float())
+    H = big[:, :2 * 384]                                   # row stride 784 elements
+    _check(H, None, "strided fp32")
+
+
+def test_moe_down_projection_input(cuda_device):
+    """The MoE FFN's down-projection input: the gate+up GEMM output of the routed rows."""
+    c = synth.moe_case(seed=5, device=cuda_device, tokens=256, experts=16, N=2 * 256, K=512)
+    D = c["D"].clone()
+    fg.fp8_grouped_gemm_nt_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["m_indices"])
+    torch.cuda.synchronize()
+    live = c["m_indices"] >= 0
+    H = torch.where(live[:, None], D, torch.zeros_like(D))   # padding rows of D were never written
+    _check(H, c["m_indices"], "moe down input")
+
+
+def test_rejects_bad_arguments(cuda_device):
+    H = torch.zeros(4, 200, dtype=torch.bfloat16, device=cuda_device)
+    with pytest.raises(ValueError):
+        fg.swiglu_quantize_1x128(H)                          # F = 100 is not a multiple of 128
