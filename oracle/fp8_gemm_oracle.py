@@ -358,3 +358,28 @@ def swiglu_quantize_1x128(h: np.ndarray, m_indices=None):
         y[np.asarray(m_indices)[:y.shape[0]] < 0] = 0.0
     q, s = quantize_1x128(y)
     return q, s, y
+
+
+# ------------------------------------------------------------------ TN layout (dense)
+# The pages list the NT, TN, NN and TT memory layouts of the dense call (es.news.hada.io/
+# topic?id=19459, "Interfaz GEMM y restricciones de layout"; fp8_gemm_{nt,nn,tn,tt}).
+# TN: A stored [K, M] and B stored [K, N] (K the strided axis of both), D = A^T B. The
+# scales keep their logical meaning: one per (m, 128-K block) for A in sa [K/128, >=M],
+# one per 128x128 block for B in sb [ceil(N/128), K/128]; BF16 output, one rounding.
+def gemm_tn(A_km, sa, B_kn, sb):
+    """Dense TN GEMM. Returns (bf16 bits uint16 [M, N], float64 S [M, N])."""
+    A = np.asarray(A_km, dtype=np.uint8)
+    B = np.asarray(B_kn, dtype=np.uint8)
+    K, M = A.shape
+    K2, N = B.shape
+    assert K == K2 and K % BLOCK == 0
+    sa = np.asarray(sa, dtype=np.float32)
+    sb = np.asarray(sb, dtype=np.float32)
+    S = np.zeros((M, N), dtype=np.float64)
+    for kb in range(K // BLOCK):
+        a = decode_e4m3(A[kb * BLOCK:(kb + 1) * BLOCK])          # [128, M]
+        b = decode_e4m3(B[kb * BLOCK:(kb + 1) * BLOCK])          # [128, N]
+        P = a.T @ b                                              # exact block partial
+        s = sa[kb, :M].astype(np.float64)[:, None] * sb[np.arange(N) // BLOCK, kb].astype(np.float64)[None, :]
+        S += P * s
+    return bf16_bits_rne(S), S
