@@ -195,6 +195,25 @@ int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dense GEMM in the TN layout: D = A^T B with A stored [K][M] and B stored [K][N]
+ * (the pages list the NT, TN, NN and TT layouts of the dense call, fp8_gemm_{nt,nn,
+ * tn,tt}: es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout").
+ * The scales keep their meaning and layouts from fp8_gemm_nt: sa [K/128][ld_sa] (one
+ * per m per 128-K block), sb [ceil(N/128)][K/128] (one per 128x128 block); BF16 D [M][N]
+ * rounded to nearest even once.
+ *   A   e4m3 [K][lda], lda >= M, lda % 16 == 0, lda <= 2^24, 16-byte aligned.
+ *   B   e4m3 [K][ldb], ldb >= N, same rules.
+ *   sa  ld_sa >= M, ld_sa % 4 == 0; sb contiguous; both 4-byte aligned.
+ *   D   BF16 [M][ldd], ldd >= N, 2-byte aligned (8-byte stores when ldd % 4 == 0 and D
+ *       is 8-byte aligned).
+ * M >= 0 (0: nothing to do), N > 0, K > 0 and a multiple of 128. Errors as for
+ * fp8_gemm_nt; the call needs no workspace.
+ */
+int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                const void* B, int64_t ldb, const float* sb,
+                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+
+/*
  * K-grouped TN GEMM, the MoE weight-gradient form: grouping along K with M and N
  * fixed (es.news.hada.io/topic?id=19459, "Dense y Grouped GEMM",
  * k_grouped_fp8_gemm_tn_contiguous; "TN" is the layout pair of D = A^T B, "Interfaz

@@ -66,6 +66,7 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked_ue8m0": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
@@ -330,6 +331,29 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
         _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
         _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
     _check(st, name)
+    return D
+
+
+def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+    """Dense TN GEMM: D [M, N] (bfloat16) = A^T B with A [K, M] and B [K, N] (e4m3 bytes,
+    K-major, unit inner stride), sa [K/128, >=M] and sb [ceil(N/128), K/128] as for
+    fp8_gemm_nt."""
+    A, B = _bytes_view(A), _bytes_view(B)
+    dev = D.device
+    _require(dev.type == "cuda" and all(t.device == dev for t in (A, sa, B, sb)), "tensors must share one GPU")
+    _require(A.dim() == 2 and B.dim() == 2 and A.stride(-1) == 1 and B.stride(-1) == 1,
+             "A and B must be 2-D [K, M] / [K, N] with unit inner stride")
+    _require(D.dtype == torch.bfloat16 and D.dim() == 2 and D.stride(-1) == 1, "D must be bfloat16 [M, N]")
+    M, N = D.shape
+    K = A.shape[0]
+    _require(B.shape[0] == K and A.shape[1] >= M and B.shape[1] >= N, "A must be [K, >=M] and B [K, >=N]")
+    _require(sa.dtype == torch.float32 and sa.shape[0] == K // 128 and sa.stride(-1) == 1 and sa.shape[1] >= M,
+             "sa must be float32 [K/128, >=M]")
+    _require(sb.dtype == torch.float32 and sb.is_contiguous() and sb.numel() == ((N + 127) // 128) * (K // 128),
+             "sb must be contiguous float32 [ceil(N/128), K/128]")
+    st = lib().fp8_gemm_tn(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                           _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
+    _check(st, "fp8_gemm_tn")
     return D
 
 

@@ -575,6 +575,46 @@ int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const flo
                       true);
 }
 
+int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
+  if (M < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
+  // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
+  if (lda < M || lda % 16 != 0 || ldb < N || ldb % 16 != 0 || lda > (1 << 24) || ldb > (1 << 24))
+    return FP8GEMM_ERR_LAYOUT;
+  if (ld_sa < M || ld_sa % 4 != 0 || ldd < N) return FP8GEMM_ERR_LAYOUT;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 2))
+    return FP8GEMM_ERR_LAYOUT;
+  int st;
+  const int cus = effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  fp8gemm::KParams p{};
+  p.A = static_cast<const uint8_t*>(A);
+  p.sa = sa;
+  p.B = static_cast<const uint8_t*>(B);
+  p.sb = sb;
+  p.Dh = static_cast<uint16_t*>(D);
+  p.lda = lda, p.ld_sa = ld_sa, p.ldb = ldb, p.ld_sb = K / fp8gemm::kBlockK, p.ldd = ldd;
+  p.M = M, p.N = N, p.G = 1;
+  p.kb_start[0] = 0;
+  p.kb_start[1] = K / fp8gemm::kBlockK;
+  p.vec4 = (ldd % 4 == 0 && aligned(D, 8)) ? 1 : 0;
+  // the tile rule of the K-grouped call
+  const bool big = ceil_div(M, 256) * ceil_div(N, 256) >= cus;
+  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
+  p.tiles_m = (int)ceil_div(M, bm);
+  p.tiles_n = (int)ceil_div(N, bn);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  if (big)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, false, true>), dim3((unsigned)tiles), dim3(512),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, false, true>), dim3((unsigned)tiles),
+                       dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+
 int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,
                               int64_t ldq, float* sa, int64_t ld_sa, int M, int F, hipStream_t stream) {
   if (!H || !Q || !sa) return FP8GEMM_ERR_NULL;

@@ -43,6 +43,7 @@ struct KParams {
   const uint8_t* B;
   const float* sb;
   float* D;
+  uint16_t* Dh;    // BF16 output of the dense TN call (DENSE_TN instances)
   int64_t lda, ld_sa, ldb, ld_sb, ldd, d_gstride;
   int M, N, G;
   int tiles_m, tiles_n;
@@ -72,7 +73,10 @@ __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >>
 // -- one exponent per lane for its A row and one for its B row, which is exactly the
 // per-column scaling of both operands -- and accumulates it itself, so no promotion
 // VALU work is left.
-template <int WAVES_M, int WAVES_N, int TNW, int STAGES, bool E8 = false>
+// DENSE_TN instances are the dense call in the TN layout (one group over all of K): B
+// carries one scale per 128x128 block (sb [ceil(N/128)][ld_sb = K/128]) as in the NT
+// call, and the output is BF16 (round to nearest even once, from the FP32 accumulator).
+template <int WAVES_M, int WAVES_N, int TNW, int STAGES, bool E8 = false, bool DENSE_TN = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_kernel(const KParams p) {
   using namespace kg;
   constexpr int NW = WAVES_M * WAVES_N;
@@ -123,8 +127,11 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   const bool s_is_a = 64 * wave < BM;
   const int s_col = s_is_a ? m0 + 64 * wave + lane : n0 + min(64 * wave - BM, BN - 64) + lane;
   const int s_lim = (s_is_a ? p.M : p.N) - 1;
-  const float* s_src = (s_is_a ? p.sa : p.sb) + (s_col < s_lim ? s_col : s_lim);
-  const int64_t s_ld = s_is_a ? p.ld_sa : p.ld_sb;
+  const int s_c = s_col < s_lim ? s_col : s_lim;
+  // column-scale layouts advance one row per K block; the 128x128 block layout of B
+  // holds a K block's scale of column n at [n / 128][kb]
+  const float* s_src = s_is_a ? p.sa + s_c : (DENSE_TN ? p.sb + (int64_t)(s_c >> 7) * p.ld_sb : p.sb + s_c);
+  const int64_t s_ld = s_is_a ? p.ld_sa : (DENSE_TN ? 1 : p.ld_sb);
 
   const uint32_t smem_base = lds_addr(smem);
   auto issue = [&](int kb, int slot) {
@@ -230,6 +237,29 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   }
 
   // ---- epilogue: lane holds D[m][n .. n + 3] of each fragment
+  if constexpr (DENSE_TN) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int m = m0 + 64 * wm + 16 * t + li;
+      if (m >= p.M) continue;
+      uint16_t* row = p.Dh + (int64_t)m * p.ldd;
+#pragma unroll
+      for (int j = 0; j < TNW; ++j) {
+        const int n = n0 + 16 * (TNW * wn + j) + 4 * q;
+        const v4f v = acc[t][j];
+        const uint32_t lo = bf16x2_bits(v[0], v[1]), hi = bf16x2_bits(v[2], v[3]);
+        if (p.vec4 && n + 3 < p.N) {
+          *reinterpret_cast<uint2*>(row + n) = make_uint2(lo, hi);
+        } else {
+          const uint32_t w[2] = {lo, hi};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < p.N) row[n + r] = (uint16_t)(w[r >> 1] >> (16 * (r & 1)));
+        }
+      }
+    }
+    return;
+  }
   float* Dg = p.D + (int64_t)g * p.d_gstride;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
