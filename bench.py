@@ -606,6 +606,8 @@ def main():
     ap.add_argument("--ue8m0", action="store_true",
                     help="with --workload grouped or kgrouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--accumulate", action="store_true", help="with --workload kgrouped: D += A^T B")
+    ap.add_argument("--layout", choices=("nt", "tn"), default="nt",
+                    help="dense workload: tn stores A and B K-major and calls fp8_gemm_tn")
     ap.add_argument("--kg-pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="build profiles/traffic_kgrouped.json from rocprofv3 --pmc runs of --workload kgrouped")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
@@ -656,6 +658,9 @@ def main():
     dev = torch.device("cuda:0")
     shapes = parse_shapes(args.shapes) if args.shapes else CONFIG2
     ue8m0 = args.workload == "ue8m0"
+    tn = args.layout == "tn"
+    if tn and (ue8m0 or args.with_c):
+        sys.exit("--layout tn takes FP32 scales and no C")
     gemm = fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
     cases = []
     for i, (M, N, K) in enumerate(shapes):
@@ -665,6 +670,14 @@ def main():
         c["C"] = (torch.randn(M, N, generator=synth.make_generator(2500 + i, dev), device=dev) * 0.1).to(
             torch.bfloat16) if args.with_c else None
         c["cfg"] = fg.query_config(fg.KIND_DENSE, M, N, K)
+        if tn:  # the same operands stored K-major (rows padded to 16 bytes)
+            c["At"] = torch.zeros(K, (M + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+            c["Bt"] = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+            c["At"][:, :M] = c["A"].t()
+            c["Bt"][:, :N] = c["B"].t()
+            del c["A"], c["B"]
+            big = (M + 255) // 256 * ((N + 255) // 256) >= (fg.get_num_cus() or 256)
+            c["cfg"] = {"block_m": 256 if big else 128, "block_n": 256 if big else 128, "split_k": 1}
         cases.append(c)
     torch.cuda.synchronize()
 
@@ -672,7 +685,9 @@ def main():
         for i, c in enumerate(cases):
             if events is not None:
                 events[i][0].record()
-            if c["C"] is not None:
+            if tn:
+                fg.fp8_gemm_tn(c["At"], c["sa"], c["Bt"], c["sb"], c["D"])
+            elif c["C"] is not None:
                 fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
             else:
                 gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
@@ -710,7 +725,7 @@ def main():
     if os.path.exists(args.traffic_file):
         with open(args.traffic_file) as f:
             tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_source_hash() and not ue8m0 and not args.with_c:  # this very kernel only
+        if tr.get("kernel_sha") == kernel_source_hash() and not ue8m0 and not args.with_c and not tn:  # this very kernel only
             traffic = tr.get("shapes", {})
 
     total_flops = 0.0
@@ -741,13 +756,14 @@ def main():
         roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dom["gbs"] / PEAK_HBM_GBS, 4)}
     roof["traffic"] = tr["bytes_per_launch"] if tr else None
-    roof["kernel"] = "fp8_gemm_kernel M=%d N=%d K=%d tile %s split %d" % (
-        dom["M"], dom["N"], dom["K"], dom["tile"], dom["split_k"])
+    roof["kernel"] = "%s M=%d N=%d K=%d tile %s split %d" % (
+        "fp8_k_grouped_tn_kernel (dense TN)" if tn else "fp8_gemm_kernel", dom["M"], dom["N"], dom["K"], dom["tile"],
+        dom["split_k"])
     roof["avg_us"] = dom["us"]
     roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
 
     cpu = None
-    if not args.no_cpu_baseline and not ue8m0 and not args.with_c:
+    if not args.no_cpu_baseline and not ue8m0 and not args.with_c and not tn:
         cpu = cpu_baseline()
 
     out = {
@@ -755,10 +771,11 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
         "data": "synthetic",
-        "config": {"workload": "dense FP8 NT GEMM with 1x128/128x128 %s scales and BF16 output over %d "
+        "config": {"workload": "dense FP8 %s GEMM with 1x128/128x128 %s scales and BF16 output over %d "
                                "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)"
-                               % ("UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
-                               + (", D = C + A B^T with a BF16 C" if args.with_c else ""),
+                               % ("TN" if tn else "NT", "UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
+                               + (", D = C + A B^T with a BF16 C" if args.with_c else "")
+                               + (" (A and B stored K-major, fp8_gemm_tn)" if tn else ""),
                    "shapes": ["%dx%dx%d" % s for s in shapes]},
         "roofline": roof,
         "cpu_baseline": cpu,
