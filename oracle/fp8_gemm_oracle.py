@@ -383,3 +383,38 @@ def gemm_tn(A_km, sa, B_kn, sb):
         s = sa[kb, :M].astype(np.float64)[:, None] * sb[np.arange(N) // BLOCK, kb].astype(np.float64)[None, :]
         S += P * s
     return bf16_bits_rne(S), S
+
+
+# NN: A stored [M, K] (as in NT), B stored [K, N]; TT: A stored [K, M], B stored [N, K] (as
+# in NT). Same scales and output as the other layouts.
+def _gemm_any(a_rows, b_cols, M, N, K, sa, sb):
+    """Shared by gemm_nn / gemm_tt: a_rows(kb) -> decoded A block [M, 128], b_cols(kb) ->
+    decoded B block [128, N]."""
+    sa = np.asarray(sa, dtype=np.float32)
+    sb = np.asarray(sb, dtype=np.float32)
+    S = np.zeros((M, N), dtype=np.float64)
+    for kb in range(K // BLOCK):
+        P = a_rows(kb) @ b_cols(kb)                              # exact block partial
+        s = sa[kb, :M].astype(np.float64)[:, None] * sb[np.arange(N) // BLOCK, kb].astype(np.float64)[None, :]
+        S += P * s
+    return bf16_bits_rne(S), S
+
+
+def gemm_nn(A_mk, sa, B_kn, sb):
+    """Dense NN GEMM D = A B, A [M, K], B [K, N]. Returns (bf16 bits [M, N], float64 S)."""
+    A = np.asarray(A_mk, dtype=np.uint8)
+    B = np.asarray(B_kn, dtype=np.uint8)
+    (M, K), N = A.shape, B.shape[1]
+    assert B.shape[0] == K and K % BLOCK == 0
+    return _gemm_any(lambda kb: decode_e4m3(A[:, kb * BLOCK:(kb + 1) * BLOCK]),
+                     lambda kb: decode_e4m3(B[kb * BLOCK:(kb + 1) * BLOCK]), M, N, K, sa, sb)
+
+
+def gemm_tt(A_km, sa, B_nk, sb):
+    """Dense TT GEMM D = A^T B^T, A [K, M], B [N, K]. Returns (bf16 bits [M, N], float64 S)."""
+    A = np.asarray(A_km, dtype=np.uint8)
+    B = np.asarray(B_nk, dtype=np.uint8)
+    (K, M), N = A.shape, B.shape[0]
+    assert B.shape[1] == K and K % BLOCK == 0
+    return _gemm_any(lambda kb: decode_e4m3(A[kb * BLOCK:(kb + 1) * BLOCK]).T,
+                     lambda kb: decode_e4m3(B[:, kb * BLOCK:(kb + 1) * BLOCK]).T, M, N, K, sa, sb)
