@@ -214,6 +214,20 @@ int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
 
 /*
+ * The dense call in the NN and TT layouts (same passage): D = A B with A stored [M][K]
+ * (K contiguous, as in fp8_gemm_nt: lda >= K) and B stored [K][N] (ldb >= N); and
+ * D = A^T B^T with A stored [K][M] (lda >= M) and B stored [N][K] (as in fp8_gemm_nt:
+ * ldb >= K). Scales, output, alignment (leading dimensions multiples of 16, at most
+ * 2^24), shape rules and errors as for fp8_gemm_tn.
+ */
+int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                const void* B, int64_t ldb, const float* sb,
+                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                const void* B, int64_t ldb, const float* sb,
+                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+
+/*
  * K-grouped TN GEMM, the MoE weight-gradient form: grouping along K with M and N
  * fixed (es.news.hada.io/topic?id=19459, "Dense y Grouped GEMM",
  * k_grouped_fp8_gemm_tn_contiguous; "TN" is the layout pair of D = A^T B, "Interfaz

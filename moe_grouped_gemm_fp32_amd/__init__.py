@@ -67,6 +67,8 @@ _SIGS = {
     "fp8_grouped_gemm_nt_masked_ue8m0": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_gemm_tn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_nn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_tt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
@@ -334,27 +336,43 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
     return D
 
 
-def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
-    """Dense TN GEMM: D [M, N] (bfloat16) = A^T B with A [K, M] and B [K, N] (e4m3 bytes,
-    K-major, unit inner stride), sa [K/128, >=M] and sb [ceil(N/128), K/128] as for
-    fp8_gemm_nt."""
+def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream):
     A, B = _bytes_view(A), _bytes_view(B)
     dev = D.device
     _require(dev.type == "cuda" and all(t.device == dev for t in (A, sa, B, sb)), "tensors must share one GPU")
     _require(A.dim() == 2 and B.dim() == 2 and A.stride(-1) == 1 and B.stride(-1) == 1,
-             "A and B must be 2-D [K, M] / [K, N] with unit inner stride")
+             "A and B must be 2-D with unit inner stride")
     _require(D.dtype == torch.bfloat16 and D.dim() == 2 and D.stride(-1) == 1, "D must be bfloat16 [M, N]")
     M, N = D.shape
-    K = A.shape[0]
-    _require(B.shape[0] == K and A.shape[1] >= M and B.shape[1] >= N, "A must be [K, >=M] and B [K, >=N]")
+    K = A.shape[0] if a_kmajor else A.shape[1]
+    _require((A.shape[1] >= M) if a_kmajor else (A.shape[0] == M), "A does not match D's rows")
+    _require((B.shape[0] == K and B.shape[1] >= N) if b_kmajor else (B.shape[1] == K and B.shape[0] == N),
+             "B does not match K and D's columns")
     _require(sa.dtype == torch.float32 and sa.shape[0] == K // 128 and sa.stride(-1) == 1 and sa.shape[1] >= M,
              "sa must be float32 [K/128, >=M]")
     _require(sb.dtype == torch.float32 and sb.is_contiguous() and sb.numel() == ((N + 127) // 128) * (K // 128),
              "sb must be contiguous float32 [ceil(N/128), K/128]")
-    st = lib().fp8_gemm_tn(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-                           _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
-    _check(st, "fp8_gemm_tn")
+    st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                              _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
+    _check(st, name)
     return D
+
+
+def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+    """Dense TN GEMM: D [M, N] (bfloat16) = A^T B with A [K, M] and B [K, N] (e4m3 bytes,
+    K-major, unit inner stride), sa [K/128, >=M] and sb [ceil(N/128), K/128] as for
+    fp8_gemm_nt."""
+    return _dense_layout("fp8_gemm_tn", True, True, A, sa, B, sb, D, stream)
+
+
+def fp8_gemm_nn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+    """Dense NN GEMM: D = A B with A [M, K] (as for fp8_gemm_nt) and B [K, N] (K-major)."""
+    return _dense_layout("fp8_gemm_nn", False, True, A, sa, B, sb, D, stream)
+
+
+def fp8_gemm_tt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+    """Dense TT GEMM: D = A^T B^T with A [K, M] (K-major) and B [N, K] (as for fp8_gemm_nt)."""
+    return _dense_layout("fp8_gemm_tt", True, False, A, sa, B, sb, D, stream)
 
 
 MAX_K_GROUPS = 256  # groups per fp8_k_grouped_gemm_tn_contiguous call

@@ -575,12 +575,29 @@ int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const flo
                       true);
 }
 
-int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+template <bool A_KC, bool B_KC>
+void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hipStream_t stream) {
+  if (big)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, false, true, A_KC, B_KC>), dim3((unsigned)tiles),
+                       dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, false, true, A_KC, B_KC>), dim3((unsigned)tiles),
+                       dim3(256), 0, stream, p);
+}
+
+// The dense call in the TN (a_kc = b_kc = false), NN (a_kc) and TT (b_kc) layouts: a
+// K-contiguous operand is [rows][ld >= K], a K-major one [K][ld >= rows].
+int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                 const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream, bool a_kc,
+                 bool b_kc) {
   if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
   if (M < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
   // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
-  if (lda < M || lda % 16 != 0 || ldb < N || ldb % 16 != 0 || lda > (1 << 24) || ldb > (1 << 24))
+  if (lda < (a_kc ? K : M) || lda % 16 != 0 || ldb < (b_kc ? K : N) || ldb % 16 != 0 || lda > (1 << 24) ||
+      ldb > (1 << 24))
     return FP8GEMM_ERR_LAYOUT;
   if (ld_sa < M || ld_sa % 4 != 0 || ldd < N) return FP8GEMM_ERR_LAYOUT;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 2))
@@ -606,13 +623,31 @@ int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
   p.tiles_m = (int)ceil_div(M, bm);
   p.tiles_n = (int)ceil_div(N, bn);
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-  if (big)
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, false, true>), dim3((unsigned)tiles), dim3(512),
-                       0, stream, p);
+  if (a_kc)
+    launch_dense_layout<true, false>(p, big, tiles, stream);
+  else if (b_kc)
+    launch_dense_layout<false, true>(p, big, tiles, stream);
   else
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, false, true>), dim3((unsigned)tiles),
-                       dim3(256), 0, stream, p);
+    launch_dense_layout<false, false>(p, big, tiles, stream);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false);
+}
+
+int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false);
+}
+
+int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true);
 }
 
 int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,

@@ -73,10 +73,16 @@ __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >>
 // -- one exponent per lane for its A row and one for its B row, which is exactly the
 // per-column scaling of both operands -- and accumulates it itself, so no promotion
 // VALU work is left.
-// DENSE_TN instances are the dense call in the TN layout (one group over all of K): B
-// carries one scale per 128x128 block (sb [ceil(N/128)][ld_sb = K/128]) as in the NT
+// DENSE_TN instances are the dense call in another memory layout (one group over all of
+// K): B carries one scale per 128x128 block (sb [ceil(N/128)][ld_sb = K/128]) as in the NT
 // call, and the output is BF16 (round to nearest even once, from the FP32 accumulator).
-template <int WAVES_M, int WAVES_N, int TNW, int STAGES, bool E8 = false, bool DENSE_TN = false>
+// A_KC / B_KC make that operand K-contiguous ([rows][K], as in the NT call) instead of
+// K-major: its panels hold [128 rows][128 k] in the NT kernel's swizzled row layout and
+// its fragments come from two 16-byte reads per lane, with the same lane -> K order as
+// the transposing read (so the two kinds of operand combine): TN = neither, NN = A_KC,
+// TT = B_KC.
+template <int WAVES_M, int WAVES_N, int TNW, int STAGES, bool E8 = false, bool DENSE_TN = false, bool A_KC = false,
+          bool B_KC = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_kernel(const KParams p) {
   using namespace kg;
   constexpr int NW = WAVES_M * WAVES_N;
@@ -115,11 +121,21 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     const int panel = u >> 4;
     is_b[i] = panel >= LY::a_panels;
     const int half = is_b[i] ? panel - LY::a_panels : panel;
-    const int k = 8 * (u & 15) + (lane >> 3);
-    const int col = 128 * half + 16 * ((lane & 7) ^ chunk_key(k));
     const int c0 = is_b[i] ? n0 : m0, lim = is_b[i] ? p.N : p.M;
-    const int col_g = c0 + col < lim ? c0 + col : c0;   // chunks past M / N re-read the first
-    off[i] = (uint32_t)k * (uint32_t)(is_b[i] ? p.ldb : p.lda) + (uint32_t)col_g;
+    const uint32_t ld = (uint32_t)(is_b[i] ? p.ldb : p.lda);
+    if (is_b[i] ? B_KC : A_KC) {
+      // K-contiguous: LDS row position 8 (u % 16) + lane / 8 holds tile row row_at(.),
+      // whose logical 16-byte K chunk (lane % 8) ^ (row & 7) sits at position lane % 8;
+      // rows past M / N re-read the tile's first row. Offset from the tile's first row.
+      const int row = 128 * half + row_at(8 * (u & 15) + (lane >> 3));
+      const int c = (lane & 7) ^ (row & 7);
+      off[i] = (c0 + row < lim ? (uint32_t)row : 0u) * ld + (uint32_t)(16 * c);
+    } else {
+      const int k = 8 * (u & 15) + (lane >> 3);
+      const int col = 128 * half + 16 * ((lane & 7) ^ chunk_key(k));
+      const int col_g = c0 + col < lim ? c0 + col : c0;   // chunks past M / N re-read the first
+      off[i] = (uint32_t)k * ld + (uint32_t)col_g;
+    }
   }
   // scales: wave w loads entry 64 w + lane of [sa of the BM columns | sb of the BN columns];
   // waves past the BM + BN entries re-load the last sb entries into their own unused slot,
@@ -137,8 +153,8 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   auto issue = [&](int kb, int slot) {
     const uint32_t st = smem_base + slot * LY::stage;
     const int64_t krow = (int64_t)(kb0 + kb) * kBlockK;
-    const uint8_t* a_base = p.A + krow * p.lda;
-    const uint8_t* b_base = p.B + krow * p.ldb;
+    const uint8_t* a_base = A_KC ? p.A + (int64_t)m0 * p.lda + krow : p.A + krow * p.lda;
+    const uint8_t* b_base = B_KC ? p.B + (int64_t)n0 * p.ldb + krow : p.B + krow * p.ldb;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) dma16(is_b[i] ? b_base : a_base, off[i], st + (LPW * wave + i) * 1024);
     dma4v(s_src + (int64_t)(kb0 + kb) * s_ld, st + LY::s_off + wave * 256);
@@ -157,6 +173,19 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(v2i_t*)(base + r * 8 * 128));
     return v8i{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
+  };
+  // K-contiguous operand: 16-row chunk c of the tile; lane 16 q + i takes row 16 c + i,
+  // K bytes 32 q .. 32 q + 31 (logical 16-byte chunks 2q and 2q + 1)
+  auto read_frag_kc = [&](uint8_t* tile, int c) {
+    const int row = 16 * (c & 7) + li;
+    uint8_t* panel = tile + (c >> 3) * kPanel;
+    const uint4 lo = *reinterpret_cast<const uint4*>(panel + swz(row, 2 * q));
+    const uint4 hi = *reinterpret_cast<const uint4*>(panel + swz(row, 2 * q + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto frag_a = [&](uint8_t* st, int c) { return A_KC ? read_frag_kc(st, c) : read_frag(st + frag_off(c)); };
+  auto frag_b = [&](uint8_t* st, int c) {
+    return B_KC ? read_frag_kc(st + LY::b_off, c) : read_frag(st + LY::b_off + frag_off(c));
   };
 
   v4f acc[4][TNW];
@@ -184,7 +213,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     float sa_t[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      fa[t] = read_frag(st + frag_off(4 * wm + t));
+      fa[t] = frag_a(st, 4 * wm + t);
       sa_t[t] = s_a[64 * wm + 16 * t + li];
     }
     if constexpr (E8) {
@@ -199,7 +228,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
         int eb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          fb[j] = read_frag(st + LY::b_off + frag_off(TNW * wn + 4 * jh + j));
+          fb[j] = frag_b(st, TNW * wn + 4 * jh + j);
           eb[j] = (__float_as_int(s_b[16 * (TNW * wn + 4 * jh + j) + li]) >> 23) & 0xFF;
         }
 #pragma unroll
@@ -217,7 +246,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
       v4f sb_j[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fb[j] = read_frag(st + LY::b_off + frag_off(TNW * wn + 4 * jh + j));
+        fb[j] = frag_b(st, TNW * wn + 4 * jh + j);
         sb_j[j] = *reinterpret_cast<const v4f*>(s_b + 16 * TNW * wn + 16 * (4 * jh + j) + 4 * q);
       }
 #pragma unroll

@@ -1,5 +1,6 @@
-"""GPU parity of the dense TN layout (fp8_gemm_tn: D = A^T B, A [K, M], B [K, N]) against
-the CPU oracle (oracle.gemm_tn): both tile instances, ragged M / N tails with padded
+"""GPU parity of the dense TN, NN and TT layouts (fp8_gemm_tn: D = A^T B, A [K, M], B [K, N];
+fp8_gemm_nn: A [M, K], B [K, N]; fp8_gemm_tt: A [K, M], B [N, K]) against the CPU oracle
+(oracle.gemm_tn / gemm_nn / gemm_tt): both tile instances, ragged M / N tails with padded
 leading dimensions, exact integer cases bit for bit (the library's bar otherwise), a
 strided and 2-byte-aligned D, and the dominant dense shape on sampled rows."""
 import numpy as np
@@ -68,3 +69,44 @@ def test_dominant_shape_sampled(cuda_device):
     A = At[:, :M].cpu().numpy()[:, rows]
     ref, _ = oracle.gemm_tn(A, c["sa"].cpu().numpy()[:, rows], Bt[:, :N].cpu().numpy(), c["sb"].cpu().numpy())
     compare("normal", got[rows], ref, "tn 4096x7168x16384 sampled rows")
+
+
+def layout_operands(c, At, Bt, layout):
+    """(A, B) for the call and the oracle function of a layout."""
+    if layout == "nn":
+        return c["A"], Bt, fg.fp8_gemm_nn
+    return At, c["B"], fg.fp8_gemm_tt
+
+
+@pytest.mark.parametrize("layout", ["nn", "tt"])
+@pytest.mark.parametrize("kind", ["normal", "e1", "e2"])
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (65, 200, 384), (300, 520, 1280)])
+def test_nn_tt_parity(cuda_device, tile, layout, kind, M, N, K):
+    c, At, Bt = tn_case(M, N, K, 4300 + M + N + K, cuda_device, kind)
+    A, B, fn = layout_operands(c, At, Bt, layout)
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    if layout == "nn":
+        ref2, _ = oracle.gemm_nn(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), Bt[:, :N].cpu().numpy(),
+                                 c["sb"].cpu().numpy())
+    else:
+        ref2, _ = oracle.gemm_tt(At[:, :M].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(),
+                                 c["sb"].cpu().numpy())
+    assert np.array_equal(ref, ref2)
+    compare(kind, bits_of(D), ref2, f"{layout} {tile} {kind} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["nn", "tt"])
+def test_nn_tt_dominant_shape_sampled(cuda_device, layout):
+    M, N, K = 4096, 7168, 16384
+    c, At, Bt = tn_case(M, N, K, 4400, cuda_device, "normal")
+    A, B, fn = layout_operands(c, At, Bt, layout)
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24, 4401)
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy()[rows], c["sa"].cpu().numpy()[:, rows], c["B"].cpu().numpy(),
+                            c["sb"].cpu().numpy())
+    compare("normal", bits_of(D)[rows], ref, f"{layout} 4096x7168x16384 sampled rows")
