@@ -606,8 +606,9 @@ def main():
     ap.add_argument("--ue8m0", action="store_true",
                     help="with --workload grouped or kgrouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--accumulate", action="store_true", help="with --workload kgrouped: D += A^T B")
-    ap.add_argument("--layout", choices=("nt", "tn"), default="nt",
-                    help="dense workload: tn stores A and B K-major and calls fp8_gemm_tn")
+    ap.add_argument("--layout", choices=("nt", "tn", "nn", "tt"), default="nt",
+                    help="dense workload in another memory layout: the K-major operands stored [K, rows] "
+                         "and fp8_gemm_tn / fp8_gemm_nn / fp8_gemm_tt called")
     ap.add_argument("--kg-pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="build profiles/traffic_kgrouped.json from rocprofv3 --pmc runs of --workload kgrouped")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_dense_shapes.json"))
@@ -658,9 +659,10 @@ def main():
     dev = torch.device("cuda:0")
     shapes = parse_shapes(args.shapes) if args.shapes else CONFIG2
     ue8m0 = args.workload == "ue8m0"
-    tn = args.layout == "tn"
+    tn = args.layout != "nt"   # one of the other memory layouts
     if tn and (ue8m0 or args.with_c):
-        sys.exit("--layout tn takes FP32 scales and no C")
+        sys.exit("--layout %s takes FP32 scales and no C" % args.layout)
+    layout_fn = {"tn": "fp8_gemm_tn", "nn": "fp8_gemm_nn", "tt": "fp8_gemm_tt"}.get(args.layout)
     gemm = fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
     cases = []
     for i, (M, N, K) in enumerate(shapes):
@@ -670,12 +672,15 @@ def main():
         c["C"] = (torch.randn(M, N, generator=synth.make_generator(2500 + i, dev), device=dev) * 0.1).to(
             torch.bfloat16) if args.with_c else None
         c["cfg"] = fg.query_config(fg.KIND_DENSE, M, N, K)
-        if tn:  # the same operands stored K-major (rows padded to 16 bytes)
-            c["At"] = torch.zeros(K, (M + 15) // 16 * 16, dtype=torch.uint8, device=dev)
-            c["Bt"] = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=dev)
-            c["At"][:, :M] = c["A"].t()
-            c["Bt"][:, :N] = c["B"].t()
-            del c["A"], c["B"]
+        if tn:  # the same operands, those the layout makes K-major stored [K, rows] (padded to 16 bytes)
+            if args.layout in ("tn", "tt"):
+                At = torch.zeros(K, (M + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+                At[:, :M] = c["A"].t()
+                c["A"] = At
+            if args.layout in ("tn", "nn"):
+                Bt = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+                Bt[:, :N] = c["B"].t()
+                c["B"] = Bt
             big = (M + 255) // 256 * ((N + 255) // 256) >= (fg.get_num_cus() or 256)
             c["cfg"] = {"block_m": 256 if big else 128, "block_n": 256 if big else 128, "split_k": 1}
         cases.append(c)
@@ -686,7 +691,7 @@ def main():
             if events is not None:
                 events[i][0].record()
             if tn:
-                fg.fp8_gemm_tn(c["At"], c["sa"], c["Bt"], c["sb"], c["D"])
+                getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"])
             elif c["C"] is not None:
                 fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
             else:
@@ -757,7 +762,7 @@ def main():
                 "frac": round(dom["gbs"] / PEAK_HBM_GBS, 4)}
     roof["traffic"] = tr["bytes_per_launch"] if tr else None
     roof["kernel"] = "%s M=%d N=%d K=%d tile %s split %d" % (
-        "fp8_k_grouped_tn_kernel (dense TN)" if tn else "fp8_gemm_kernel", dom["M"], dom["N"], dom["K"], dom["tile"],
+        "fp8_k_grouped_tn_kernel (dense %s)" % args.layout.upper() if tn else "fp8_gemm_kernel", dom["M"], dom["N"], dom["K"], dom["tile"],
         dom["split_k"])
     roof["avg_us"] = dom["us"]
     roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
@@ -773,9 +778,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense FP8 %s GEMM with 1x128/128x128 %s scales and BF16 output over %d "
                                "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)"
-                               % ("TN" if tn else "NT", "UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
+                               % (args.layout.upper(), "UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
                                + (", D = C + A B^T with a BF16 C" if args.with_c else "")
-                               + (" (A and B stored K-major, fp8_gemm_tn)" if tn else ""),
+                               + (" (%s)" % layout_fn if tn else ""),
                    "shapes": ["%dx%dx%d" % s for s in shapes]},
         "roofline": roof,
         "cpu_baseline": cpu,
