@@ -20,6 +20,15 @@
  * The pages name the scaling scheme but not its block sizes; 1x128 (A) and
  * 128x128 (B) are the DeepSeek-V3 granularity they refer to.
  *
+ * Beside the three NT calls (each also in a UE8M0-scale form *_ue8m0 and an
+ * accumulate form *_c, D = C + A B^T), the library has the dense call in the TN, NN
+ * and TT layouts (fp8_gemm_tn / _nn / _tt), the K-grouped TN GEMM of the MoE weight
+ * gradient with FP32 output (fp8_k_grouped_gemm_tn_contiguous, also _ue8m0), and the
+ * 1x128 activation quantiser (fp8_quantize_1x128, fp8_swiglu_quantize_1x128); each
+ * declaration below states its own operation and layouts where they differ from the
+ * conventions here (the leading-dimension rule, for one, follows each operand's
+ * layout).
+ *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
  *    allocates, frees or synchronises, and never reads device memory from the host.
