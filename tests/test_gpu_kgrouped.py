@@ -183,3 +183,22 @@ def test_ue8m0_full_size_sampled(cuda_device, M, N):
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, 12, replace=False)]))
     cols = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.choice(N, 12, replace=False)]))
     check(c, D, rows=rows, cols=cols, what=f"ue8m0 full {M}x{N}")
+
+
+def test_all_groups_empty(cuda_device, tile):
+    """Every group of length 0 (called through the C ABI with valid buffers, none of them
+    read): D is zero-filled, or left as it was when accumulating."""
+    import ctypes
+    c = synth.k_grouped_case([128], 96, 80, seed=9950, device=cuda_device)
+    D = torch.full((3, 96, 80), 7.0, device=cuda_device)
+    ks = (ctypes.c_int32 * 3)(0, 0, 0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(cuda_device).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    for accumulate, want in ((1, 7.0), (0, 0.0)):
+        st = fg.lib().fp8_k_grouped_gemm_tn_contiguous(
+            P(c["A"]), c["A"].stride(0), P(c["sa"]), c["sa"].stride(0), P(c["B"]), c["B"].stride(0), P(c["sb"]),
+            c["sb"].stride(0), P(D), D.stride(1), D.stride(0), ctypes.cast(ks, ctypes.c_void_p), 3, 96, 80,
+            accumulate, stream)
+        assert st == 0, fg.status_string(st)
+        torch.cuda.synchronize()
+        assert torch.all(D == want)

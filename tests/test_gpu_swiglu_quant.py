@@ -105,3 +105,18 @@ def test_rejects_bad_arguments(cuda_device):
     H = torch.zeros(4, 200, dtype=torch.bfloat16, device=cuda_device)
     with pytest.raises(ValueError):
         fg.swiglu_quantize_1x128(H)                          # F = 100 is not a multiple of 128
+
+
+def test_empty_and_single_row(cuda_device):
+    # M = 0 through the C ABI (torch gives zero-element tensors a null pointer): a no-op
+    import ctypes
+    big = torch.zeros(4, 256, dtype=torch.bfloat16, device=cuda_device)
+    Qb = torch.zeros(4, 128, dtype=torch.uint8, device=cuda_device)
+    sab = torch.ones(1, 4, dtype=torch.float32, device=cuda_device)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = fg.lib().fp8_swiglu_quantize_1x128(P(big), 256, fg.QUANT_BF16, None, P(Qb), 128, P(sab), 4, 0, 128,
+                                            ctypes.c_void_p(torch.cuda.current_stream(cuda_device).cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and torch.all(Qb == 0) and torch.all(sab == 1)
+    g = synth.make_generator(1500, cuda_device)
+    _check(torch.randn(1, 256, generator=g, device=cuda_device).to(torch.bfloat16), None, "one row")

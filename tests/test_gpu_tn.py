@@ -110,3 +110,31 @@ def test_nn_tt_dominant_shape_sampled(cuda_device, layout):
     ref, _ = oracle.gemm_nt(c["A"].cpu().numpy()[rows], c["sa"].cpu().numpy()[:, rows], c["B"].cpu().numpy(),
                             c["sb"].cpu().numpy())
     compare("normal", bits_of(D)[rows], ref, f"{layout} 4096x7168x16384 sampled rows")
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+def test_degenerate_shapes(cuda_device, layout):
+    """M = 0 launches nothing; one K block and a single output row or column still match."""
+    fns = {"tn": fg.fp8_gemm_tn, "nn": fg.fp8_gemm_nn, "tt": fg.fp8_gemm_tt}
+    for M, N, K in [(1, 8, 128), (200, 1, 256)]:
+        c, At, Bt = tn_case(M, N, K, 4500 + M + N, cuda_device, "e1")
+        A = c["A"] if layout == "nn" else At
+        B = c["B"] if layout == "tt" else Bt
+        D = c["D"].clone()
+        fns[layout](A, c["sa"], B, c["sb"], D)
+        torch.cuda.synchronize()
+        ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(),
+                                c["sb"].cpu().numpy())
+        compare("e1", bits_of(D), ref, f"{layout} {M}x{N}x{K}")
+    # M = 0 through the C ABI (torch gives zero-element tensors a null pointer): a no-op
+    import ctypes
+    c, At, Bt = tn_case(16, 16, 128, 4600, cuda_device, "e1")
+    A = c["A"] if layout == "nn" else At
+    B = c["B"] if layout == "tt" else Bt
+    D = c["D"].clone()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = getattr(fg.lib(), "fp8_gemm_" + layout)(P(A), A.stride(0), P(c["sa"]), c["sa"].stride(0), P(B), B.stride(0),
+                                                 P(c["sb"]), P(D), D.stride(0), 0, 16, 128,
+                                                 ctypes.c_void_p(torch.cuda.current_stream(cuda_device).cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and torch.equal(D.view(torch.int16), c["D"].view(torch.int16))
