@@ -660,8 +660,8 @@ def main():
     shapes = parse_shapes(args.shapes) if args.shapes else CONFIG2
     ue8m0 = args.workload == "ue8m0"
     tn = args.layout != "nt"   # one of the other memory layouts
-    if tn and (ue8m0 or args.with_c):
-        sys.exit("--layout %s takes FP32 scales and no C" % args.layout)
+    if tn and args.with_c:
+        sys.exit("--layout %s takes no C" % args.layout)
     layout_fn = {"tn": "fp8_gemm_tn", "nn": "fp8_gemm_nn", "tt": "fp8_gemm_tt"}.get(args.layout)
     gemm = fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
     cases = []
@@ -691,7 +691,7 @@ def main():
             if events is not None:
                 events[i][0].record()
             if tn:
-                getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"])
+                getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"], ue8m0=ue8m0)
             elif c["C"] is not None:
                 fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
             else:

@@ -22,7 +22,7 @@
  *
  * Beside the three NT calls (each also in a UE8M0-scale form *_ue8m0 and an
  * accumulate form *_c, D = C + A B^T), the library has the dense call in the TN, NN
- * and TT layouts (fp8_gemm_tn / _nn / _tt), the K-grouped TN GEMM of the MoE weight
+ * and TT layouts (fp8_gemm_tn / _nn / _tt, also _ue8m0), the K-grouped TN GEMM of the MoE weight
  * gradient with FP32 output (fp8_k_grouped_gemm_tn_contiguous, also _ue8m0), and the
  * 1x128 activation quantiser (fp8_quantize_1x128, fp8_swiglu_quantize_1x128); each
  * declaration below states its own operation and layouts where they differ from the
@@ -235,6 +235,21 @@ int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 const void* B, int64_t ldb, const float* sb,
                 void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+
+/*
+ * The TN, NN and TT calls with UE8M0 scale factors: the same operations, layouts and
+ * errors, with every sa and sb value an exact power of two 2^(e-127), 1 <= e <= 254,
+ * held as FP32 (see fp8_gemm_nt_ue8m0); the block-scaled MFMA applies them.
+ */
+int fp8_gemm_tn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const void* B, int64_t ldb, const float* sb,
+                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+int fp8_gemm_nn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const void* B, int64_t ldb, const float* sb,
+                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+int fp8_gemm_tt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const void* B, int64_t ldb, const float* sb,
+                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
 
 /*
  * K-grouped TN GEMM, the MoE weight-gradient form: grouping along K with M and N

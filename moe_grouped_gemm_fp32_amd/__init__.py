@@ -69,6 +69,9 @@ _SIGS = {
     "fp8_gemm_tn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
     "fp8_gemm_nn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
     "fp8_gemm_tt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_tn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_nn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_tt_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
@@ -358,21 +361,24 @@ def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream):
     return D
 
 
-def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
+                ue8m0: bool = False):
     """Dense TN GEMM: D [M, N] (bfloat16) = A^T B with A [K, M] and B [K, N] (e4m3 bytes,
     K-major, unit inner stride), sa [K/128, >=M] and sb [ceil(N/128), K/128] as for
     fp8_gemm_nt."""
-    return _dense_layout("fp8_gemm_tn", True, True, A, sa, B, sb, D, stream)
+    return _dense_layout("fp8_gemm_tn" + ("_ue8m0" if ue8m0 else ""), True, True, A, sa, B, sb, D, stream)
 
 
-def fp8_gemm_nn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+def fp8_gemm_nn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
+                ue8m0: bool = False):
     """Dense NN GEMM: D = A B with A [M, K] (as for fp8_gemm_nt) and B [K, N] (K-major)."""
-    return _dense_layout("fp8_gemm_nn", False, True, A, sa, B, sb, D, stream)
+    return _dense_layout("fp8_gemm_nn" + ("_ue8m0" if ue8m0 else ""), False, True, A, sa, B, sb, D, stream)
 
 
-def fp8_gemm_tt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None):
+def fp8_gemm_tt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
+                ue8m0: bool = False):
     """Dense TT GEMM: D = A^T B^T with A [K, M] (K-major) and B [N, K] (as for fp8_gemm_nt)."""
-    return _dense_layout("fp8_gemm_tt", True, False, A, sa, B, sb, D, stream)
+    return _dense_layout("fp8_gemm_tt" + ("_ue8m0" if ue8m0 else ""), True, False, A, sa, B, sb, D, stream)
 
 
 MAX_K_GROUPS = 256  # groups per fp8_k_grouped_gemm_tn_contiguous call

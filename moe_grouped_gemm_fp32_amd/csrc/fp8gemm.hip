@@ -578,21 +578,32 @@ int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const flo
 }  // extern "C"
 
 namespace {
-template <bool A_KC, bool B_KC>
+template <bool E8, bool A_KC, bool B_KC>
 void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hipStream_t stream) {
   if (big)
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, false, true, A_KC, B_KC>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, E8, true, A_KC, B_KC>), dim3((unsigned)tiles),
                        dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, false, true, A_KC, B_KC>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, E8, true, A_KC, B_KC>), dim3((unsigned)tiles),
                        dim3(256), 0, stream, p);
+}
+template <bool E8>
+void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hipStream_t stream, bool a_kc,
+                         bool b_kc) {
+  if (a_kc)
+    launch_dense_layout<E8, true, false>(p, big, tiles, stream);
+  else if (b_kc)
+    launch_dense_layout<E8, false, true>(p, big, tiles, stream);
+  else
+    launch_dense_layout<E8, false, false>(p, big, tiles, stream);
 }
 
 // The dense call in the TN (a_kc = b_kc = false), NN (a_kc) and TT (b_kc) layouts: a
-// K-contiguous operand is [rows][ld >= K], a K-major one [K][ld >= rows].
+// K-contiguous operand is [rows][ld >= K], a K-major one [K][ld >= rows]. e8: UE8M0
+// (power-of-two) scales applied by the block-scaled MFMA.
 int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                  const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream, bool a_kc,
-                 bool b_kc) {
+                 bool b_kc, bool e8 = false) {
   if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
   if (M < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
   // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
@@ -623,12 +634,10 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   p.tiles_m = (int)ceil_div(M, bm);
   p.tiles_n = (int)ceil_div(N, bn);
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-  if (a_kc)
-    launch_dense_layout<true, false>(p, big, tiles, stream);
-  else if (b_kc)
-    launch_dense_layout<false, true>(p, big, tiles, stream);
+  if (e8)
+    launch_dense_layout<true>(p, big, tiles, stream, a_kc, b_kc);
   else
-    launch_dense_layout<false, false>(p, big, tiles, stream);
+    launch_dense_layout<false>(p, big, tiles, stream, a_kc, b_kc);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 }  // namespace
@@ -648,6 +657,21 @@ int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                 const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
   return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true);
+}
+
+int fp8_gemm_tn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false, true);
+}
+
+int fp8_gemm_nn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false, true);
+}
+
+int fp8_gemm_tt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true, true);
 }
 
 int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,

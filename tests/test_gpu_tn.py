@@ -138,3 +138,20 @@ def test_degenerate_shapes(cuda_device, layout):
                                                  ctypes.c_void_p(torch.cuda.current_stream(cuda_device).cuda_stream))
     torch.cuda.synchronize()
     assert st == 0 and torch.equal(D.view(torch.int16), c["D"].view(torch.int16))
+
+
+# ---- UE8M0 (power-of-two) scales through fp8_gemm_{tn,nn,tt}_ue8m0: the oracle is the
+# same layout definition on the same power-of-two FP32 scale values
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+@pytest.mark.parametrize("kind", ["pow2", "e1"])
+@pytest.mark.parametrize("M,N,K", [(65, 200, 384), (300, 520, 1280)])
+def test_ue8m0_parity(cuda_device, tile, layout, kind, M, N, K):
+    c, At, Bt = tn_case(M, N, K, 4700 + M + N + K, cuda_device, kind)
+    A = c["A"] if layout == "nn" else At
+    B = c["B"] if layout == "tt" else Bt
+    fn = {"tn": fg.fp8_gemm_tn, "nn": fg.fp8_gemm_nn, "tt": fg.fp8_gemm_tt}[layout]
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D, ue8m0=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    compare("e1" if kind == "e1" else "normal", bits_of(D), ref, f"{layout} ue8m0 {tile} {kind} {M}x{N}x{K}")
