@@ -207,3 +207,46 @@ def test_k_grouped_argument_validation_without_launch():
     import torch
     if not torch.cuda.is_available():
         assert call() == -5 and call(ks=[0, 0]) == -5   # valid: stops at the device check
+
+
+@pytest.mark.parametrize("name,a_kc,b_kc", [("fp8_gemm_tn", False, False), ("fp8_gemm_nn", True, False),
+                                            ("fp8_gemm_tt", False, True), ("fp8_gemm_tn_ue8m0", False, False),
+                                            ("fp8_gemm_nn_ue8m0", True, False), ("fp8_gemm_tt_ue8m0", False, True)])
+def test_layout_argument_validation_without_launch(name, a_kc, b_kc):
+    """Every argument error is reported before any device call; the leading-dimension rule
+    follows each operand's layout (K-contiguous: ld >= K, K-major: ld >= rows)."""
+    M, N, K = 4096, 7168, 2048
+    fn = getattr(fg.lib(), name)
+    base = dict(A=1 << 20, lda=K if a_kc else M, sa=1 << 20, ld_sa=M, B=1 << 20, ldb=K if b_kc else N,
+                sb=1 << 20, D=1 << 20, ldd=N, M=M, N=N, K=K)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return fn(P(a["A"]), a["lda"], P(a["sa"]), a["ld_sa"], P(a["B"]), a["ldb"], P(a["sb"]), P(a["D"]), a["ldd"],
+                  a["M"], a["N"], a["K"], None)
+
+    assert call(A=0) == -1 and call(sb=0) == -1 and call(D=0) == -1
+    assert call(K=100) == -2 and call(N=0) == -2 and call(M=-1) == -2
+    assert call(lda=(K if a_kc else M) - 16) == -3 and call(ldb=(K if b_kc else N) + 8) == -3
+    assert call(ld_sa=M - 4) == -3 and call(ldd=N - 1) == -3 and call(A=(1 << 20) + 8) == -3
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == -5   # valid: stops at the device check
+
+
+def test_swiglu_quantize_argument_validation_without_launch():
+    fn = fg.lib().fp8_swiglu_quantize_1x128
+    base = dict(H=1 << 20, ldh=4096, dt=0, mi=None, Q=1 << 20, ldq=2048, sa=1 << 20, ld_sa=64, M=64, F=2048)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return fn(P(a["H"]), a["ldh"], a["dt"], P(a["mi"]) if a["mi"] else None, P(a["Q"]), a["ldq"], P(a["sa"]),
+                  a["ld_sa"], a["M"], a["F"], None)
+
+    assert call(H=0) == -1 and call(Q=0) == -1 and call(sa=0) == -1
+    assert call(F=100) == -2 and call(F=0) == -2 and call(M=-1) == -2
+    assert call(ldh=4000) == -3 and call(ldh=4100) == -3 and call(dt=7) == -3 and call(ldq=2047) == -3
+    assert call(ld_sa=60) == -3 and call(mi=(1 << 20) + 2) == -3 and call(H=(1 << 20) + 8) == -3
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == -5 and call(M=0) == -5
