@@ -22,7 +22,7 @@
  *
  * Beside the three NT calls (each also in a UE8M0-scale form *_ue8m0 and an
  * accumulate form *_c, D = C + A B^T), the library has the dense call in the TN, NN
- * and TT layouts (fp8_gemm_tn / _nn / _tt, also _ue8m0), the K-grouped TN GEMM of the MoE weight
+ * and TT layouts (fp8_gemm_tn / _nn / _tt, also _ue8m0 and _c), the K-grouped TN GEMM of the MoE weight
  * gradient with FP32 output (fp8_k_grouped_gemm_tn_contiguous, also _ue8m0), and the
  * 1x128 activation quantiser (fp8_quantize_1x128, fp8_swiglu_quantize_1x128); each
  * declaration below states its own operation and layouts where they differ from the
@@ -235,6 +235,24 @@ int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 const void* B, int64_t ldb, const float* sb,
                 void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+
+/*
+ * The TN, NN and TT calls in the accumulate form D = C + A B (the pages' naming of every
+ * GEMM; see fp8_gemm_nt_c): C is BF16 with D's shape, row stride ldc >= N, 2-byte
+ * aligned (8-byte loads when ldc % 4 == 0 and C is 8-byte aligned), added in FP32 to the
+ * accumulator before the one rounding; C may be D itself (in-place accumulation), any
+ * other overlap with D is not allowed. Otherwise as fp8_gemm_tn / _nn / _tt;
+ * FP8GEMM_ERR_NULL for a NULL C, FP8GEMM_ERR_LAYOUT for ldc < N or a misaligned C.
+ */
+int fp8_gemm_tn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                  const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
+                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+int fp8_gemm_nn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                  const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
+                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                  const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
+                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
 
 /*
  * The TN, NN and TT calls with UE8M0 scale factors: the same operations, layouts and

@@ -603,7 +603,7 @@ void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hip
 // (power-of-two) scales applied by the block-scaled MFMA.
 int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                  const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream, bool a_kc,
-                 bool b_kc, bool e8 = false) {
+                 bool b_kc, bool e8 = false, const void* C = nullptr, int64_t ldc = 0) {
   if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
   if (M < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
   // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
@@ -613,11 +613,15 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   if (ld_sa < M || ld_sa % 4 != 0 || ldd < N) return FP8GEMM_ERR_LAYOUT;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 2))
     return FP8GEMM_ERR_LAYOUT;
+  if (C && (ldc < N || !aligned(C, 2))) return FP8GEMM_ERR_LAYOUT;
   int st;
   const int cus = effective_cus(true, &st);
   if (st != FP8GEMM_OK) return st;
   if (M == 0) return FP8GEMM_OK;
   fp8gemm::KParams p{};
+  p.C = static_cast<const uint16_t*>(C);
+  p.ldc = ldc;
+  p.c_vec = (C && ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
   p.A = static_cast<const uint8_t*>(A);
   p.sa = sa;
   p.B = static_cast<const uint8_t*>(B);
@@ -657,6 +661,27 @@ int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                 const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
   return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true);
+}
+
+int fp8_gemm_tn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                  const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
+                  hipStream_t stream) {
+  if (!C) return FP8GEMM_ERR_NULL;
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false, false, C, ldc);
+}
+
+int fp8_gemm_nn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                  const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
+                  hipStream_t stream) {
+  if (!C) return FP8GEMM_ERR_NULL;
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false, false, C, ldc);
+}
+
+int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                  const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
+                  hipStream_t stream) {
+  if (!C) return FP8GEMM_ERR_NULL;
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true, false, C, ldc);
 }
 
 int fp8_gemm_tn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,

@@ -43,7 +43,10 @@ struct KParams {
   const uint8_t* B;
   const float* sb;
   float* D;
-  uint16_t* Dh;    // BF16 output of the dense TN call (DENSE_TN instances)
+  uint16_t* Dh;    // BF16 output of the dense layout calls (DENSE_TN instances)
+  const uint16_t* C;  // dense layout calls: optional BF16 addend of D = C + A B (may be Dh)
+  int64_t ldc;
+  int c_vec;          // 1: C rows allow 8-byte loads (ldc % 4 == 0, C 8-byte aligned)
   int64_t lda, ld_sa, ldb, ld_sb, ldd, d_gstride;
   int M, N, G;
   int tiles_m, tiles_n;
@@ -75,7 +78,8 @@ __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >>
 // VALU work is left.
 // DENSE_TN instances are the dense call in another memory layout (one group over all of
 // K): B carries one scale per 128x128 block (sb [ceil(N/128)][ld_sb = K/128]) as in the NT
-// call, and the output is BF16 (round to nearest even once, from the FP32 accumulator).
+// call, and the output is BF16 (round to nearest even once, from the FP32 accumulator,
+// after adding the optional BF16 C of D = C + A B).
 // A_KC / B_KC make that operand K-contiguous ([rows][K], as in the NT call) instead of
 // K-major: its panels hold [128 rows][128 k] in the NT kernel's swizzled row layout and
 // its fragments come from two 16-byte reads per lane, with the same lane -> K order as
@@ -275,7 +279,19 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
 #pragma unroll
       for (int j = 0; j < TNW; ++j) {
         const int n = n0 + 16 * (TNW * wn + j) + 4 * q;
-        const v4f v = acc[t][j];
+        v4f v = acc[t][j];
+        if (p.C) {  // each lane reads the C elements of exactly the D elements it writes
+          const uint16_t* crow = p.C + (int64_t)m * p.ldc + n;
+          if (p.c_vec && n + 3 < p.N) {
+            const uint2 cw = *reinterpret_cast<const uint2*>(crow);
+            v[0] += bf16_value(cw.x & 0xFFFF), v[1] += bf16_value(cw.x >> 16);
+            v[2] += bf16_value(cw.y & 0xFFFF), v[3] += bf16_value(cw.y >> 16);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < p.N) v[r] += bf16_value(crow[r]);
+          }
+        }
         const uint32_t lo = bf16x2_bits(v[0], v[1]), hi = bf16x2_bits(v[2], v[3]);
         if (p.vec4 && n + 3 < p.N) {
           *reinterpret_cast<uint2*>(row + n) = make_uint2(lo, hi);

@@ -155,3 +155,29 @@ def test_ue8m0_parity(cuda_device, tile, layout, kind, M, N, K):
     torch.cuda.synchronize()
     ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
     compare("e1" if kind == "e1" else "normal", bits_of(D), ref, f"{layout} ue8m0 {tile} {kind} {M}x{N}x{K}")
+
+
+# ---- D = C + A B in the three layouts (fp8_gemm_{tn,nn,tt}_c): the oracle is the NT
+# accumulate form on the same operands (the layout oracles equal the NT one, pinned)
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+@pytest.mark.parametrize("kind", ["normal", "e1"])
+def test_c_parity_and_in_place(cuda_device, tile, layout, kind):
+    M, N, K = 300, 520, 1280
+    c, At, Bt = tn_case(M, N, K, 4800 + len(layout) + len(kind), cuda_device, kind)
+    A = c["A"] if layout == "nn" else At
+    B = c["B"] if layout == "tt" else Bt
+    fn = {"tn": fg.fp8_gemm_tn, "nn": fg.fp8_gemm_nn, "tt": fg.fp8_gemm_tt}[layout]
+    g = synth.make_generator(4900, cuda_device)
+    if kind == "e1":  # multiples of 1/4 within +-64: C + (an E1 sum) is exact in FP32
+        C = (torch.randint(-256, 257, (M, N), generator=g, device=cuda_device).float() / 4).to(torch.bfloat16)
+    else:
+        C = (torch.randn(M, N, generator=g, device=cuda_device) * 0.5).to(torch.bfloat16)
+    ref, _ = oracle.gemm_nt_c(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(),
+                              c["sb"].cpu().numpy(), bits_of(C))
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D, C=C)
+    torch.cuda.synchronize()
+    compare(kind, bits_of(D), ref, f"{layout} C {tile} {kind}")
+    fn(A, c["sa"], B, c["sb"], C, C=C)                      # in place: C is D
+    torch.cuda.synchronize()
+    compare(kind, bits_of(C), ref, f"{layout} C in place {tile} {kind}")
