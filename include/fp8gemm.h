@@ -46,9 +46,13 @@
  *  - Preconditions on device data (cannot be checked from the host): no e4m3 NaN
  *    codes in live rows; m_indices / masked_m as documented per call.
  *  - Split-K workspace: optional. When `workspace` is NULL or smaller than
- *    fp8_gemm_workspace_size(...), the call runs without split-K. A workspace must
- *    be zero-filled before its first use; every call leaves it zeroed again (its
- *    counters self-reset). Calls that run concurrently must not share a workspace.
+ *    fp8_gemm_workspace_size(...), the call runs without split-K (or with fewer
+ *    split tiles). Layout: the first 16 KiB hold 4096 int32 arrival counters, the
+ *    rest FP32 partial sums. The counters must be zero before the workspace's first
+ *    use (zero-fill the buffer once); every call that completes leaves them zero
+ *    again. The partials need no initial value. So one workspace may serve any
+ *    sequence of calls of any shapes, one after another on a stream. Calls that may
+ *    run concurrently (other streams) must not share a workspace.
  */
 #ifndef FP8GEMM_H_
 #define FP8GEMM_H_
@@ -87,7 +91,10 @@ typedef struct {
 } fp8gemm_config_t;
 
 /*
- * Dense D[M, N] = A[M, K] . B[N, K]^T.
+ * Dense D[M, N] = A[M, K] . B[N, K]^T: the normal (non-grouped) GEMM of the pages
+ * (bquan.live post 9429818, "¿Cómo usarlo?"; es.news.hada.io/topic?id=19459,
+ * "Interfaz GEMM y restricciones de layout": fp8_gemm_nt, the NT layout, FP32 LHS
+ * scales in a transposed layout).
  *   A  e4m3 [M, K] row-major, row stride lda.
  *   sa fp32 [K/128][ld_sa]: sa[kb * ld_sa + m] scales row m of K block kb
  *      (the transposed, M-contiguous layout), ld_sa >= M.
@@ -187,7 +194,9 @@ int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The M-grouped calls with UE8M0 scale factors: the same operations, layouts,
+ * The M-grouped calls with UE8M0 scale factors (the UE8M0 scale format of
+ * es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout", on the
+ * grouped layouts of "Dense y Grouped GEMM"): the same operations, layouts,
  * preconditions and errors as fp8_grouped_gemm_nt_contiguous and
  * fp8_grouped_gemm_nt_masked, with every scale an exact power of two held as FP32
  * (see fp8_gemm_nt_ue8m0): the block-scaled MFMA applies them.
@@ -223,7 +232,9 @@ int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
 
 /*
- * The dense call in the NN and TT layouts (same passage): D = A B with A stored [M][K]
+ * The dense call in the NN and TT layouts (es.news.hada.io/topic?id=19459, "Interfaz
+ * GEMM y restricciones de layout" and "Dense y Grouped GEMM": fp8_gemm_{nt, nn, tn,
+ * tt}): D = A B with A stored [M][K]
  * (K contiguous, as in fp8_gemm_nt: lda >= K) and B stored [K][N] (ldb >= N); and
  * D = A^T B^T with A stored [K][M] (lda >= M) and B stored [N][K] (as in fp8_gemm_nt:
  * ldb >= K). Scales, output, alignment (leading dimensions multiples of 16, at most
@@ -238,7 +249,8 @@ int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
 
 /*
  * The TN, NN and TT calls in the accumulate form D = C + A B (the pages' naming of every
- * GEMM; see fp8_gemm_nt_c): C is BF16 with D's shape, row stride ldc >= N, 2-byte
+ * GEMM, es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout"; see
+ * fp8_gemm_nt_c): C is BF16 with D's shape, row stride ldc >= N, 2-byte
  * aligned (8-byte loads when ldc % 4 == 0 and C is 8-byte aligned), added in FP32 to the
  * accumulator before the one rounding; C may be D itself (in-place accumulation), any
  * other overlap with D is not allowed. Otherwise as fp8_gemm_tn / _nn / _tt;
@@ -255,7 +267,8 @@ int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                   void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
 
 /*
- * The TN, NN and TT calls with UE8M0 scale factors: the same operations, layouts and
+ * The TN, NN and TT calls with UE8M0 scale factors (both from es.news.hada.io/topic?
+ * id=19459, "Interfaz GEMM y restricciones de layout"): the same operations, layouts and
  * errors, with every sa and sb value an exact power of two 2^(e-127), 1 <= e <= 254,
  * held as FP32 (see fp8_gemm_nt_ue8m0); the block-scaled MFMA applies them.
  */
@@ -306,7 +319,9 @@ int fp8_k_grouped_gemm_tn_contiguous(const void* A, int64_t lda, const float* sa
                                      hipStream_t stream);
 
 /*
- * The K-grouped TN GEMM with UE8M0 scale factors: the same operation, layouts,
+ * The K-grouped TN GEMM with UE8M0 scale factors (the call of es.news.hada.io/topic?
+ * id=19459, "Dense y Grouped GEMM", with the UE8M0 scale format of "Interfaz GEMM y
+ * restricciones de layout"): the same operation, layouts,
  * preconditions and errors as fp8_k_grouped_gemm_tn_contiguous, with every sa and sb
  * value an exact power of two 2^(e-127), 1 <= e <= 254, held as FP32 (see
  * fp8_gemm_nt_ue8m0). gfx950's block-scaled MFMA applies them: each lane passes the
@@ -365,37 +380,67 @@ int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int
                               int64_t ldq, float* sa, int64_t ld_sa, int M, int F, hipStream_t stream);
 
 /* Bytes of split-K workspace the call with these sizes may use (0 = never splits).
- * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked). */
+ * Splitting K is this library's choice for MI355X (the pages' Hopper kernels do not
+ * split K), so this utility has no counterpart on the pages.
+ * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked).
+ * expected_m is the masked call's tiling hint, taken here so that the answer is
+ * computed by the same planner with the same arguments as the call itself (the
+ * masked call never splits K today, so it returns 0 for FP8GEMM_KIND_MASKED; the
+ * argument is ignored for the other kinds). The size includes the 16 KiB counter
+ * block described in the conventions above. */
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m);
 
 /* Configuration the library would use for a call (no launch, no device access
- * when fp8_gemm_set_num_cus() has been given a value). Returns FP8GEMM_OK. */
+ * when fp8_gemm_set_num_cus() has been given a value). Returns FP8GEMM_OK. The
+ * pages' configuration printout (es.news.hada.io/topic?id=19459, "Utilidades y
+ * variables de entorno": DG_PRINT_CONFIGS prints the configuration chosen per shape)
+ * as a query; FP8GEMM_PRINT_CONFIGS=1 prints it at every call. */
 int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m,
                           size_t workspace_bytes, fp8gemm_config_t* out);
 
-/* Force the tile configuration of later calls (tuning and tests): block_m,
+/* Force the tile configuration of later calls (tuning and tests; a utility of this
+ * library with no counterpart on the pages): block_m,
  * block_n, split_k and full_tiles (clamped to the tile count; 0 splits every
  * tile) are used, grid and num_units are ignored. NULL restores
  * automatic selection. Not thread-safe; process-wide.
- * Returns FP8GEMM_ERR_CONFIG for a tile shape that has no kernel. */
+ * Returns FP8GEMM_ERR_CONFIG for a tile shape that has no kernel; a later call
+ * returns FP8GEMM_ERR_CONFIG if the forced plan splits more than 4096 tiles. */
 int fp8_gemm_force_config(const fp8gemm_config_t* cfg);
 
-/* Cap on the compute units the persistent grid is sized for (DeepGEMM's
- * set_num_sms analog, "Utilidades y variables de entorno"). n <= 0 restores the
- * device's own count. get returns the value in effect (0 if none is known yet). */
+/* Cap on the compute units the persistent grid is sized for: the analog of
+ * DeepGEMM's set_num_sms / get_num_sms (es.news.hada.io/topic?id=19459, "Utilidades
+ * y variables de entorno": set and query the maximum number of SMs to use). n <= 0
+ * restores the device's own count. get returns the value in effect (0 if none is
+ * known yet). */
 int fp8_gemm_set_num_cus(int n);
 int fp8_gemm_get_num_cus(void);
 
-/* Row alignment of each expert segment in the contiguous layout: 128. */
+/* Row alignment of each expert segment in the contiguous layout, and of each group's
+ * K length in the K-grouped call: 128. The pages require every expert segment of the
+ * contiguous layout to be aligned to the GEMM's M block size and expose that
+ * alignment through get_mk_alignment_for_contiguous_layout (es.news.hada.io/topic?
+ * id=19459, "Dense y Grouped GEMM"; the same getter, group-level M/K alignment, in
+ * "Utilidades y variables de entorno"). Here it is fixed at one scale block (128
+ * rows), which every tile height used by the contiguous call divides, so a tile
+ * never spans two experts. No setter: the value cannot change. */
 int fp8_gemm_get_mk_alignment_for_contiguous_layout(void);
 
-/* Smallest valid ld_sa for `rows` rows: rows rounded up to a multiple of 4. */
+/* Smallest valid ld_sa for `rows` rows: rows rounded up to a multiple of 4. The
+ * analog of DeepGEMM's get_tma_aligned_size (es.news.hada.io/topic?id=19459,
+ * "Utilidades y variables de entorno": the alignment size the LHS scale layout
+ * needs; "Interfaz GEMM y restricciones de layout": the LHS scales must be aligned
+ * and transposed). Here the activation scales are [K/128][ld_sa] FP32 and the
+ * kernels read them in 16-byte groups, so ld_sa must be a multiple of 4. rows <= 0
+ * gives 0. */
 int64_t fp8_gemm_scale_ld(int64_t rows);
 
-/* Number of output tiles of an M x N output cut into block_m x block_n tiles. */
+/* Number of output tiles of an M x N output cut into block_m x block_n tiles: the
+ * count behind the pages' unaligned-block argument (deepep.org/zh/deepgemm, 核心优化技术,
+ * 非对齐块大小: the number of tiles decides how many SMs get work). */
 int64_t fp8_gemm_num_tiles(int64_t M, int64_t N, int block_m, int block_n);
 
-/* Static description of a status code. */
+/* Static description of a status code (a utility of this library with no counterpart
+ * on the pages). */
 const char* fp8_gemm_status_string(int status);
 
 #ifdef __cplusplus

@@ -322,8 +322,8 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
     _require(sa.dim() == 3 and sa.shape[0] == G and sa.shape[1] == K // 128 and sa.shape[2] >= M_max,
              "sa must be [G, K/128, >=M_max]")
     _require(tuple(sb.shape) == (G, (N + 127) // 128, K // 128), "sb must be [G, ceil(N/128), K/128]")
-    _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev,
-             "masked_m must be an int32 [G] device tensor")
+    _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev
+             and masked_m.is_contiguous(), "masked_m must be a contiguous int32 [G] device tensor")
     wp, wb = _ws(workspace)
     if C is not None:
         _require(not ue8m0, "C is supported with FP32 scales")

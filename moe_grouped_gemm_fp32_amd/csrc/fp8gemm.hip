@@ -100,9 +100,19 @@ bool has_kernel(int bm, int bn) {
   return false;
 }
 
-size_t split_ws_bytes(int64_t tiles, int split, int bm, int bn) {
+// Split-K workspace layout: a fixed block of kMaxSplitTiles int32 arrival counters at
+// offset 0, then the FP32 partials [split tile][split][BM*BN]. The counters sit at the
+// same place whatever the plan, so calls of different shapes (different tiles and
+// splits) can share one workspace: every counter is zero before a call and is zero again
+// when it completes (the last arrival resets it). The partials need no initial value:
+// each call writes a partial before any workgroup reads it.
+constexpr int64_t kMaxSplitTiles = 4096;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int32_t);  // 16 KiB
+static_assert(kCounterBytes % 256 == 0, "partials start 256-byte aligned");
+
+size_t split_ws_bytes(int64_t split_tiles, int split, int bm, int bn) {
   if (split <= 1) return 0;
-  return (size_t)tiles * split * bm * bn * sizeof(float) + (size_t)tiles * sizeof(int32_t);
+  return kCounterBytes + (size_t)split_tiles * split * bm * bn * sizeof(float);
 }
 
 // Cost model of the planner (microseconds, fitted to timings on MI355X): per tile
@@ -158,7 +168,8 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     auto consider = [&](const Variant& v, int64_t tiles, int split, int64_t full) {
       const int kbps = (int)ceil_div(num_kb, split);
       const int64_t split_tiles = split > 1 ? tiles - full : 0;
-      if (split > 1 && split_ws_bytes(split_tiles, split, v.bm, v.bn) > ws_avail) return;
+      if (split > 1 && (split_tiles > kMaxSplitTiles || split_ws_bytes(split_tiles, split, v.bm, v.bn) > ws_avail))
+        return;
       const UnitCost c = unit_cost(v.bm, v.bn);
       const double reduce =
           split > 1 ? kSplitUnitUs + kSplitReadUsPerKB * (split - 1) * (v.bm * v.bn * 4.0 / 1024.0) : 0.0;
@@ -209,7 +220,7 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (kind == FP8GEMM_KIND_MASKED ? G : 1);
   pl.full = pl.split > 1 && kind != FP8GEMM_KIND_MASKED ? std::min<int64_t>(pl.full, tiles) : tiles;
   pl.ws_bytes = split_ws_bytes(tiles - pl.full, pl.split, pl.bm, pl.bn);
-  if (pl.split > 1 && pl.ws_bytes > ws_avail && !g_forced) {
+  if (pl.split > 1 && (pl.ws_bytes > ws_avail || tiles - pl.full > kMaxSplitTiles) && !g_forced) {
     pl.split = 1;
     pl.kbps = num_kb;
     pl.full = tiles;
@@ -293,6 +304,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   const size_t ws_avail = workspace ? workspace_bytes : 0;
   Plan pl = choose(kind, rows, N, K, G, expected_m, cus, ws_avail);
   if (!has_kernel(pl.bm, pl.bn)) return FP8GEMM_ERR_CONFIG;
+  if (pl.split > 1 && pl.units - pl.full > kMaxSplitTiles * pl.split) return FP8GEMM_ERR_CONFIG;
   if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
   maybe_print(name, rows, N, K, G, pl);
   p.N = N;
@@ -310,10 +322,8 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.vec_store = (p.ldd % 8 == 0 && aligned(p.D, 16)) ? 2 : (p.ldd % 4 == 0 && aligned(p.D, 8)) ? 1 : 0;
   p.c_vec = p.C && p.ldc % 8 == 0 && aligned(p.C, 16) ? 1 : 0;
   if (pl.split > 1) {
-    const int64_t split_tiles = (pl.units - pl.full) / pl.split;
-    p.ws = static_cast<float*>(workspace);
-    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                            (size_t)split_tiles * pl.split * pl.bm * pl.bn * sizeof(float));
+    p.counters = static_cast<int32_t*>(workspace);
+    p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   }
   if (pl.units == 0) return FP8GEMM_OK;
   return launch(pl, p, stream, e8) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;

@@ -322,19 +322,6 @@ def k_grouped_tn(A, sa, B, sb, ks, D_in=None, rows=None, cols=None):
     return T.astype(np.float32), T           # float64 -> float32 rounds to nearest even
 
 
-def k_grouped_tn_abs(A, sa, B, sb, ks, rows=None, cols=None):
-    """sum_kb |s_kb| sum_k |A B|: the magnitude that bounds the rounding error of any
-    FP32 evaluation of k_grouped_tn (same shapes as its result)."""
-    a = E4M3_TABLE_ABS_CODES[np.asarray(A, dtype=np.uint8)]
-    b = E4M3_TABLE_ABS_CODES[np.asarray(B, dtype=np.uint8)]
-    return k_grouped_tn(a, np.abs(np.asarray(sa, np.float32)), b, np.abs(np.asarray(sb, np.float32)),
-                        ks, None, rows, cols)[1]
-
-
-# code of |value| for every e4m3 code (sign bit cleared; NaN codes kept)
-E4M3_TABLE_ABS_CODES = (np.arange(256) & 0x7F).astype(np.uint8)
-
-
 # ------------------------------------------------------------ SwiGLU + 1x128 quantisation
 # The MoE FFN's step between its two GEMMs is SwiGLU (es.news.hada.io/topic?id=19459,
 # "Mega MoE": linear 1, SwiGLU, linear 2); its output is the down projection's A operand,

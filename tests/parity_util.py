@@ -68,5 +68,13 @@ def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
     return np.unique(np.clip(np.array(fixed + list(extra)), 0, max(M - 1, 0)))
 
 
+def forced_workspace_bytes(kind, M, N, K, G, tile, full_tiles=0):
+    """Workspace bytes of a call under a forced (block_m, block_n, split_k) plan, as the
+    library computes it (at least 16 bytes, so a buffer can always be allocated)."""
+    import moe_grouped_gemm_fp32_amd as fg
+    with fg.force_config(*tile, full_tiles=full_tiles):
+        return max(16, fg.workspace_size(kind, M, N, K, G))
+
+
 def host(c, *keys):
     return [c[k].cpu().numpy() if isinstance(c[k], torch.Tensor) else c[k] for k in keys]

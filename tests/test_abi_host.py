@@ -250,3 +250,31 @@ def test_swiglu_quantize_argument_validation_without_launch():
     import torch
     if not torch.cuda.is_available():
         assert call() == -5 and call(M=0) == -5
+
+
+PAGE_CITATION = re.compile(r"es\.news\.hada\.io|bquan\.live|deepep\.org|kirim\.ai|GeekNews topic")
+
+
+def declaration_comments():
+    """(function name, text of the comment block that documents it) for every function the
+    header declares; declarations that follow one another share the comment above them."""
+    text = open(HEADER).read()
+    out, last_comment = [], ""
+    pos = 0
+    for m in re.finditer(r"/\*.*?\*/|^\s*(?:const\s+char\s*\*|int64_t|size_t|int)\s+(fp8_\w+)\s*\(", text, re.M | re.S):
+        if m.group(0).lstrip().startswith("/*"):
+            last_comment = m.group(0)
+        else:
+            out.append((m.group(1), last_comment))
+        pos = m.end()
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Each entry point's comment names the page passage that defines its operation, or says
+    that it is a utility of this library with no counterpart on the pages."""
+    decls = declaration_comments()
+    assert {n for n, _ in decls} == set(declared_functions())
+    flat = [(n, " ".join(c.replace("*", " ").split())) for n, c in decls]
+    missing = [n for n, c in flat if not (PAGE_CITATION.search(c) or "no counterpart on the pages" in c)]
+    assert not missing, "declarations without a citation: %s" % missing

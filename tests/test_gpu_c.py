@@ -9,7 +9,7 @@ import torch
 import moe_grouped_gemm_fp32_amd as fg
 import oracle
 import synth
-from parity_util import SENT, bits_of, compare, host, sample_rows
+from parity_util import SENT, bits_of, compare, forced_workspace_bytes, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,7 @@ def run(c, C, tile=None, D=None):
     M, N, K = c["M"], c["N"], c["K"]
     nbytes = fg.workspace_size(fg.KIND_DENSE, M, N, K)
     if tile is not None and tile[2] > 1:
-        t = fg.num_tiles(M, N, tile[0], tile[1])
-        nbytes = t * tile[2] * tile[0] * tile[1] * 4 + t * 4
+        nbytes = forced_workspace_bytes(fg.KIND_DENSE, M, N, K, 1, tile)
     work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
     if tile is None:
         fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work, C=C)

@@ -9,13 +9,14 @@ import torch
 import moe_grouped_gemm_fp32_amd as fg
 import oracle
 import synth
-from parity_util import SENT, assert_bit_exact, bits_of, compare, host, sample_rows
+from parity_util import SENT, assert_bit_exact, bits_of, compare, forced_workspace_bytes, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
 TILES = [(64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1),
          (64, 64, 2), (128, 64, 3), (128, 128, 4), (256, 128, 2), (128, 256, 3)]
 CONFIG2_NK = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]
+COUNTER_BYTES = 16384  # the workspace's leading block of split-K arrival counters
 
 
 def run_dense(c, forced=None, ws=True):
@@ -25,8 +26,7 @@ def run_dense(c, forced=None, ws=True):
     if ws:
         nbytes = fg.workspace_size(fg.KIND_DENSE, M, N, K)
         if forced is not None and forced[2] > 1:
-            tiles = fg.num_tiles(M, N, forced[0], forced[1])
-            nbytes = tiles * forced[2] * forced[0] * forced[1] * 4 + tiles * 4
+            nbytes = forced_workspace_bytes(fg.KIND_DENSE, M, N, K, 1, forced)
         work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
     if forced is None:
         fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
@@ -70,10 +70,7 @@ def test_split_k_is_deterministic_and_workspace_self_resets(cuda_device):
         fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
         torch.cuda.synchronize()
         outs.append(bits_of(D))
-        cfg = fg.query_config(fg.KIND_DENSE, 64, 2112, 7168)
-        tiles = cfg["num_units"] // cfg["split_k"]
-        counters = work[tiles * cfg["split_k"] * cfg["block_m"] * cfg["block_n"] * 4:][: tiles * 4]
-        assert int(counters.count_nonzero()) == 0, "split-K counters must be left at zero"
+        assert int(work[:COUNTER_BYTES].count_nonzero()) == 0, "split-K counters must be left at zero"
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     # without a workspace the call runs unsplit and agrees within tolerance
     D = c["D"].clone()
@@ -83,6 +80,36 @@ def test_split_k_is_deterministic_and_workspace_self_resets(cuda_device):
     ref, _ = oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(2112))
     compare("normal", bits_of(D)[rows], ref, "unsplit")
     compare("normal", outs[0][rows], ref, "split")
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_one_workspace_shared_by_different_split_plans(cuda_device, order):
+    """Two shapes whose plans differ (tile, split count and number of split tiles) run one
+    after the other through one workspace, in both orders, twice: the counters sit at a
+    fixed place, so neither call sees the other's partials as counters."""
+    shapes = [(64, 2112, 7168), (64, 7168, 2048), (128, 24576, 1536)]
+    if order:
+        shapes = shapes[::-1]
+    plans = [fg.query_config(fg.KIND_DENSE, *s) for s in shapes]
+    assert all(p["split_k"] > 1 for p in plans), plans
+    assert len({(p["block_m"], p["block_n"], p["split_k"], p["num_units"]) for p in plans}) == len(plans)
+    nbytes = max(fg.workspace_size(fg.KIND_DENSE, *s) for s in shapes)
+    work = torch.zeros(nbytes, dtype=torch.uint8, device=cuda_device)
+    cases = [synth.dense_case(M, N, K, seed=4100 + i, device=cuda_device, a_std=1.0, b_std=0.02)
+             for i, (M, N, K) in enumerate(shapes)]
+    refs = []
+    for (M, N, K), c in zip(shapes, cases):
+        rows = sample_rows(M, 10, N + K)
+        refs.append((rows, oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))[0]))
+    for rep in range(2):
+        for (M, N, K), c, (rows, ref) in zip(shapes, cases, refs):
+            D = c["D"].clone()
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+            torch.cuda.synchronize()
+            bits = bits_of(D)
+            assert not np.any(bits == SENT), f"{M}x{N}x{K} pass {rep}: an output tile was not written"
+            compare("normal", bits[rows], ref, f"shared workspace {M}x{N}x{K} pass {rep}")
+            assert int(work[:COUNTER_BYTES].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("M", [64, 128, 4096])
@@ -163,9 +190,8 @@ def test_whole_tiles_then_split_tiles(cuda_device, tile, full):
     ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
     whole, _ = run_dense(c, forced=(tile[0], tile[1], 1))
     split_all, _ = run_dense(c, forced=tile)
-    tiles = fg.num_tiles(M, N, tile[0], tile[1])
-    ws = torch.zeros(max(16, (tiles - full) * tile[2] * tile[0] * tile[1] * 4 + (tiles - full) * 4),
-                     dtype=torch.uint8, device=cuda_device)
+    ws = torch.zeros(forced_workspace_bytes(fg.KIND_DENSE, M, N, K, 1, tile, full), dtype=torch.uint8,
+                     device=cuda_device)
     for rep in range(2):
         D = synth.sentinel_output((M, N), cuda_device)
         with fg.force_config(*tile, full_tiles=full):

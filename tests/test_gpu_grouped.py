@@ -8,7 +8,7 @@ import torch
 import moe_grouped_gemm_fp32_amd as fg
 import oracle
 import synth
-from parity_util import SENT, assert_bit_exact, bits_of, compare, host, sample_rows
+from parity_util import SENT, assert_bit_exact, bits_of, compare, forced_workspace_bytes, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -18,8 +18,7 @@ def run_contig(c, forced=None):
     M, N, K, G = c["M"], c["N"], c["K"], c["G"]
     nbytes = fg.workspace_size(fg.KIND_CONTIGUOUS, M, N, K, G)
     if forced is not None and forced[2] > 1:
-        tiles = fg.num_tiles(M, N, forced[0], forced[1])
-        nbytes = tiles * forced[2] * forced[0] * forced[1] * 4 + tiles * 4
+        nbytes = forced_workspace_bytes(fg.KIND_CONTIGUOUS, M, N, K, G, forced)
     work = torch.zeros(nbytes, dtype=torch.uint8, device=D.device) if nbytes else None
     if forced is None:
         fg.fp8_grouped_gemm_nt_contiguous(c["A"], c["sa"], c["B"], c["sb"], D, c["m_indices"], work)
@@ -138,10 +137,14 @@ def test_config4_masked_full_size_sampled(cuda_device, G, N, K):
     rows = np.unique(np.concatenate([[0, 1, 178], np.random.default_rng(G).choice(179, 6, replace=False)]))
     ref, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm, d_bits(c), rows, np.arange(N))
     compare("normal", bits_of(D)[:, rows], ref, f"config4 G={G} N={N}")
-    last = np.array([v - 1 for v in mm])
+    # per group: rows in [179, masked_m[g]) (the live rows beyond the common prefix,
+    # in the later live tiles), including the last live row
+    rng = np.random.default_rng(100 + G)
     for g in range(G):
-        r1, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm, d_bits(c), [last[g]], np.arange(N))
-        compare("normal", bits_of(D)[g, last[g]], r1[g, 0], f"config4 last live row group {g}")
+        tail = np.arange(179, mm[g])
+        pick = np.unique(np.concatenate([rng.choice(tail, min(4, len(tail)), replace=False), [mm[g] - 1]]))
+        r1, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm, d_bits(c), pick, np.arange(N))
+        compare("normal", bits_of(D)[g, pick], r1[g], f"config4 rows {list(pick)} of group {g}")
 
 
 def test_config5_moe_ffn_pair(cuda_device):

@@ -10,7 +10,7 @@ import torch
 import moe_grouped_gemm_fp32_amd as fg
 import oracle
 import synth
-from parity_util import SENT, assert_bit_exact, bits_of, compare, host, sample_rows
+from parity_util import SENT, assert_bit_exact, bits_of, compare, forced_workspace_bytes, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +23,7 @@ def run(c, tile=None):
     M, N, K = c["M"], c["N"], c["K"]
     nbytes = fg.workspace_size(fg.KIND_DENSE, M, N, K)
     if tile is not None and tile[2] > 1:
-        t = fg.num_tiles(M, N, tile[0], tile[1])
-        nbytes = t * tile[2] * tile[0] * tile[1] * 4 + t * 4
+        nbytes = forced_workspace_bytes(fg.KIND_DENSE, M, N, K, 1, tile)
     work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
     if tile is None:
         fg.fp8_gemm_nt_ue8m0(c["A"], c["sa"], c["B"], c["sb"], D, work)
@@ -89,8 +88,7 @@ def _contig(c, tile, ue8m0=True):
     M, N, K, G = c["M"], c["N"], c["K"], c["G"]
     nbytes = fg.workspace_size(fg.KIND_CONTIGUOUS, M, N, K, G)
     if tile is not None and tile[2] > 1:
-        t = fg.num_tiles(M, N, tile[0], tile[1])
-        nbytes = t * tile[2] * tile[0] * tile[1] * 4 + t * 4
+        nbytes = forced_workspace_bytes(fg.KIND_CONTIGUOUS, M, N, K, G, tile)
     work = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=D.device)
     args = (c["A"], c["sa"], c["B"], c["sb"], D, c["m_indices"], work)
     if tile is None:
