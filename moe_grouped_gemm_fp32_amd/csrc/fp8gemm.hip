@@ -229,7 +229,13 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   pl.units = pl.full + (tiles - pl.full) * pl.split;
   const int64_t cap = (int64_t)cus * kOccupancy;
   int64_t grid = std::min<int64_t>(pl.units, cap);
-  if (grid > fp8gemm::kNumXcd) grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;  // keep XCD mapping
+  // A grid-stride loop keeps each workgroup on one XCD (workgroup b runs on XCD b % 8)
+  // only if the grid is a multiple of 8. When every unit has a workgroup of its own (one
+  // round), no rounding: rounding 231 units down to 224 workgroups would run 7 of them
+  // in a second round. Masked calls learn their unit count on the device, so they
+  // always round.
+  if ((pl.units > cap || kind == FP8GEMM_KIND_MASKED) && grid > fp8gemm::kNumXcd)
+    grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;
   pl.grid = (int)std::max<int64_t>(grid, 1);
   return pl;
 }

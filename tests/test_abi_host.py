@@ -107,6 +107,12 @@ def test_planner_invariants_on_dense_shapes(cus256, M, N, K):
     if tiles < 64 and nkb >= 16:
         assert s > 1 and full == 0 and cfg["num_units"] >= 128
     assert cfg["grid"] <= cfg["num_units"] and cfg["grid"] <= 512
+    # one round when the units fit on the CUs (no unit waits for a second round);
+    # otherwise a multiple of 8, so the grid-stride loop keeps each workgroup's XCD
+    if cfg["num_units"] <= 256:
+        assert cfg["grid"] == cfg["num_units"]
+    else:
+        assert cfg["grid"] % 8 == 0
     ws = fg.workspace_size(fg.KIND_DENSE, M, N, K)
     assert (ws > 0) == (s > 1)
     if s > 1:
