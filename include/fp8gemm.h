@@ -109,6 +109,28 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fp8_gemm_nt for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same operation,
+ * layouts and errors as fp8_gemm_nt, without the workspace arguments: the split-K
+ * partials and arrival counters live in a scratch array inside the library, one copy
+ * per device, of fp8_gemm_noalloc_scratch_bytes() bytes (32 MiB + 16 KiB), held from the
+ * first call on a device until the process ends. The call allocates nothing (no
+ * hipMalloc, no allocating library routine); the first call on a device looks the
+ * array up and clears its counter block with a small kernel on `stream`; every call
+ * that completes leaves the counters zero again. The planner fits its split-K plan into
+ * the scratch; a forced configuration (fp8_gemm_force_config) whose plan needs more
+ * returns FP8GEMM_ERR_WORKSPACE before any launch. All calls on one GPU share its
+ * scratch: calls that may overlap in time (other streams, other host threads) race and
+ * must not be issued; calls in order on one stream are safe.
+ */
+int fp8_gemm_nt_noalloc(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
+                        const void* B, int64_t ldb, const float* sb,
+                        void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+/* Size in bytes of the per-device scratch of fp8_gemm_nt_noalloc (the same for every
+ * device; a constant of the library), for the callers that cannot allocate. */
+size_t fp8_gemm_noalloc_scratch_bytes(void);
+
+/*
  * D = C + A B^T (the pages' naming convention for every GEMM: fp8_gemm_nt computes
  * D = C + A @ B.T; es.news.hada.io/topic?id=19459, "Interfaz GEMM y restricciones de
  * layout"). The three calls below are fp8_gemm_nt, fp8_grouped_gemm_nt_contiguous and

@@ -24,7 +24,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "fp8_gemm_nt", "fp8_gemm_nt_ue8m0", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
+    "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "noalloc_scratch_bytes", "fp8_gemm_nt_ue8m0", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
     "workspace_size", "make_workspace", "query_config", "force_config", "set_num_cus",
     "get_num_cus", "get_mk_alignment_for_contiguous_layout", "scale_ld", "num_tiles",
     "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED", "quantize_1x128",
@@ -80,6 +80,8 @@ _SIGS = {
     "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
+    "fp8_gemm_nt_noalloc": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_noalloc_scratch_bytes": (_SZ, []),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_swiglu_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_gemm_query_config": (_INT, [_INT, _INT, _INT, _INT, _INT, _INT, _SZ, ctypes.POINTER(Config)]),
@@ -193,6 +195,27 @@ def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Te
                            _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt")
     return D
+
+
+def fp8_gemm_nt_noalloc(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """fp8_gemm_nt without a workspace argument, for callers that cannot allocate: the
+    split-K scratch is the library's own per-device array (noalloc_scratch_bytes()).
+    Calls that overlap in time on one GPU must not be issued (they share the scratch)."""
+    A, B, dev = _common(A, sa, B, sb, D, 0)
+    M, K = A.shape
+    N = B.shape[0]
+    _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
+    st = lib().fp8_gemm_nt_noalloc(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+                                   _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
+    _check(st, "fp8_gemm_nt_noalloc")
+    return D
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().fp8_gemm_noalloc_scratch_bytes())
 
 
 def fp8_gemm_nt_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,

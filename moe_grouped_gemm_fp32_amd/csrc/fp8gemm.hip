@@ -32,7 +32,8 @@ constexpr int kDefaultCus = 256;
 
 struct DeviceInfo {
   int cus = 0;
-  int status = 1;  // 1 = not queried, FP8GEMM_OK or FP8GEMM_ERR_DEVICE
+  int status = 1;          // 1 = not queried, FP8GEMM_OK or FP8GEMM_ERR_DEVICE
+  void* scratch = nullptr;  // device address of this device's copy of `scratch` (set up on first use)
 };
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_dev_mutex;
@@ -74,6 +75,13 @@ int effective_cus(bool need_device, int* status) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Split-K scratch of fp8_gemm_nt_noalloc, for callers that cannot allocate: one copy per
+// device, held until the process ends. Its first kCounterBytes are the arrival counters
+// (the workspace layout below), the rest holds FP32 partials. In host code `scratch`
+// names only a host-side stand-in: kernels get the device address that
+// hipGetSymbolAddress returns (cached per device in DeviceInfo::scratch).
+constexpr size_t kScratchPartialBytes = (size_t)32 << 20;  // covers every plan of the dense configurations
+
 
 struct Plan {
   int bm = 128, bn = 128, split = 1, kbps = 1, tiles_m = 0, tiles_n = 0;
@@ -109,6 +117,34 @@ bool has_kernel(int bm, int bn) {
 constexpr int64_t kMaxSplitTiles = 4096;
 constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int32_t);  // 16 KiB
 static_assert(kCounterBytes % 256 == 0, "partials start 256-byte aligned");
+
+constexpr size_t kScratchBytes = kCounterBytes + kScratchPartialBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Device address of the current device's scratch. On a device's first call it is
+// looked up once (hipGetSymbolAddress, with that device current) and its counter block
+// is cleared by a small kernel on `stream` (a kernel, not a memset, so the call may be
+// captured into a graph); every later call that completes leaves the counters zero.
+int scratch_for_current_device(void** out, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8GEMM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& d = g_devices[dev];
+  if (!d.scratch) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP8GEMM_ERR_DEVICE;
+    hipLaunchKernelGGL(zero_words, dim3(16), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                       (int)(kCounterBytes / sizeof(uint32_t)));
+    if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
+    d.scratch = ptr;
+  }
+  *out = d.scratch;
+  return FP8GEMM_OK;
+}
 
 size_t split_ws_bytes(int64_t split_tiles, int split, int bm, int bn) {
   if (split <= 1) return 0;
@@ -411,6 +447,26 @@ int fp8_gemm_nt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, cons
   p.M = M;
   return run(FP8GEMM_KIND_DENSE, "dense", p, M, N, K, 1, 0, workspace, workspace_bytes, stream);
 }
+
+int fp8_gemm_nt_noalloc(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                        const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
+  const int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  int dst;
+  effective_cus(true, &dst);
+  if (dst != FP8GEMM_OK) return dst;
+  void* ws = nullptr;
+  const int sst = scratch_for_current_device(&ws, stream);
+  if (sst != FP8GEMM_OK) return sst;
+  Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
+  p.M = M;
+  // the planner fits its split-K plan into the scratch; a forced plan that needs more
+  // is rejected with FP8GEMM_ERR_WORKSPACE before any launch
+  return run(FP8GEMM_KIND_DENSE, "dense noalloc", p, M, N, K, 1, 0, ws, kScratchBytes, stream);
+}
+
+size_t fp8_gemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int fp8_gemm_nt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                   const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,

@@ -79,6 +79,13 @@ def test_valid_call_without_gpu_reports_device_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _dense() == -5
+    mk = lambda v: P(v)
+    na = fg.lib().fp8_gemm_nt_noalloc
+    assert na(mk(1 << 20), 7168, mk(1 << 20), 64, mk(1 << 20), 7168, mk(1 << 20), mk(1 << 20), 2112, 64, 2112, 7168,
+              None) == -5
+    assert na(None, 7168, mk(1 << 20), 64, mk(1 << 20), 7168, mk(1 << 20), mk(1 << 20), 2112, 64, 2112, 7168,
+              None) == -1
+    assert fg.noalloc_scratch_bytes() == (32 << 20) + 16384
 
 
 @pytest.fixture
@@ -278,9 +285,11 @@ def declaration_comments():
 
 def test_every_declaration_cites_its_passage():
     """Each entry point's comment names the page passage that defines its operation, or says
-    that it is a utility of this library with no counterpart on the pages."""
+    that it is a utility of this library with no counterpart on the pages, or (the
+    no-allocation variant) names the callers it is for: those that cannot allocate."""
     decls = declaration_comments()
     assert {n for n, _ in decls} == set(declared_functions())
     flat = [(n, " ".join(c.replace("*", " ").split())) for n, c in decls]
-    missing = [n for n, c in flat if not (PAGE_CITATION.search(c) or "no counterpart on the pages" in c)]
+    missing = [n for n, c in flat if not (PAGE_CITATION.search(c) or "no counterpart on the pages" in c
+                                           or "cannot allocate" in c)]
     assert not missing, "declarations without a citation: %s" % missing
