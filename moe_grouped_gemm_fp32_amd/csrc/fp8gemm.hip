@@ -276,29 +276,42 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   return pl;
 }
 
-template <int I, bool MASKED, bool E8 = false, bool HAS_C = false>
+template <int I, bool MASKED, bool E8 = false, bool HAS_C = false, bool STREAM_B = false>
 hipError_t launch_variant(const Params& p, int grid, hipStream_t stream) {
   constexpr Variant v = kVariants[I];
-  hipLaunchKernelGGL((fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED, E8, HAS_C>),
-                     dim3(grid), dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
+  hipLaunchKernelGGL(
+      (fp8gemm::fp8_gemm_kernel<v.bm, v.bn, v.waves_m, v.waves_n, v.stages, MASKED, E8, HAS_C, STREAM_B>),
+      dim3(grid), dim3(v.waves_m * v.waves_n * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// e8: power-of-two scales through the block-scaled MFMA
+// Instances with non-temporal B loads exist for the 4-wave tiles (the few-row shapes)
+// of the dense and contiguous forms.
+template <int I>
+constexpr bool kHasStreamB = kVariants[I].waves_m * kVariants[I].waves_n == 4;
+
+// e8: power-of-two scales through the block-scaled MFMA; stream_b: B tiles read once
 template <int I = 0>
-hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream, bool e8) {
+hipError_t launch(const Plan& pl, const Params& p, hipStream_t stream, bool e8, bool stream_b) {
   if constexpr (I < kNumVariants) {
     if (kVariants[I].bm == pl.bm && kVariants[I].bn == pl.bn) {
+      const bool masked = p.kind == FP8GEMM_KIND_MASKED;
+      if constexpr (kHasStreamB<I>) {
+        if (stream_b && !masked) {
+          if (e8) return launch_variant<I, false, true, false, true>(p, pl.grid, stream);
+          if (p.C) return launch_variant<I, false, false, true, true>(p, pl.grid, stream);
+          return launch_variant<I, false, false, false, true>(p, pl.grid, stream);
+        }
+      }
       if (e8)
-        return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true, true>(p, pl.grid, stream)
-                                             : launch_variant<I, false, true>(p, pl.grid, stream);
+        return masked ? launch_variant<I, true, true>(p, pl.grid, stream)
+                      : launch_variant<I, false, true>(p, pl.grid, stream);
       if (p.C)  // D = C + A B^T (FP32 scales)
-        return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true, false, true>(p, pl.grid, stream)
-                                             : launch_variant<I, false, false, true>(p, pl.grid, stream);
-      return p.kind == FP8GEMM_KIND_MASKED ? launch_variant<I, true>(p, pl.grid, stream)
-                                           : launch_variant<I, false>(p, pl.grid, stream);
+        return masked ? launch_variant<I, true, false, true>(p, pl.grid, stream)
+                      : launch_variant<I, false, false, true>(p, pl.grid, stream);
+      return masked ? launch_variant<I, true>(p, pl.grid, stream) : launch_variant<I, false>(p, pl.grid, stream);
     }
-    return launch<I + 1>(pl, p, stream, e8);
+    return launch<I + 1>(pl, p, stream, e8, stream_b);
   } else {
     return hipErrorInvalidValue;
   }
@@ -368,7 +381,9 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
     p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   }
   if (pl.units == 0) return FP8GEMM_OK;
-  return launch(pl, p, stream, e8) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+  // one tile row covers all of M (dense): each B tile is read by one unit only
+  const bool stream_b = kind == FP8GEMM_KIND_DENSE && pl.tiles_m == 1;
+  return launch(pl, p, stream, e8, stream_b) == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 
 Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,

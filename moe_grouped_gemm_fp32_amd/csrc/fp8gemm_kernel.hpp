@@ -220,6 +220,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
 }
+// The same with the non-temporal hint: lines streamed through once (an operand that no
+// other tile reads) need not displace reusable lines from the caches.
+__device__ __forceinline__ void dma16nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(uni(base)), "s"(uni((int)lds)) : "memory");
+}
 // 4-byte loads with a per-lane 64-bit address (the scale loads, whose lanes read
 // scattered rows)
 __device__ __forceinline__ void dma4v(const void* src, uint32_t lds) {
@@ -310,7 +316,12 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
 // block product by 2^(ea-127) * 2^(eb-127) and adds it to the FP32 accumulator itself:
 // the promotion needs no separate FMAs.
 // HAS_C instances add the BF16 C of D = C + A B^T in the epilogue (p.C non-null).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED, bool E8 = false, bool HAS_C = false>
+// STREAM_B instances load B with the non-temporal hint, for calls where one tile row
+// covers all of M, so that every B tile is read by exactly one work unit: streaming it
+// past the caches keeps A's lines, which every unit reads, resident (measured on the
+// few-row shapes: up to 22% faster; where B tiles are shared it is slower).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool MASKED, bool E8 = false, bool HAS_C = false,
+          bool STREAM_B = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(const Params p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int NT = NW * 64;
@@ -503,7 +514,10 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         dma16(Ag + (int64_t)i * kBlockK, a_off[q], base + (q * NW + wave) * 1024);
       } else if (q < A_INSTR + B_INSTR) {
         const int r = q - A_INSTR;
-        dma16(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
+        if constexpr (STREAM_B)
+          dma16nt(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
+        else
+          dma16(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
       } else {
         dma4v(sc_src + i * sc_step, base + A_BYTES + B_BYTES + (wave < SA_WAVES ? wave * 256 : BM * 4));
       }
