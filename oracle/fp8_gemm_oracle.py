@@ -256,6 +256,76 @@ def gemm_nt_ue8m0(A, sa_codes, B, sb_codes):
     return gemm_nt(A, ue8m0_decode(sa_codes), B, ue8m0_decode(sb_codes))
 
 
+# ------------------------------------------------------------------ packed UE8M0 scale factors
+# The newer API takes UE8M0 scale factors packed four to a 32-bit integer and offers a
+# utility that converts FP32 scale factors into the layout a kernel requires (es.news.hada.io/
+# topic?id=19459, "Interfaz GEMM y restricciones de layout": packed UE8M0, four per
+# torch.int, LHS scales aligned and transposed; "Utilidades y variables de entorno":
+# transform_sf_into_required_layout). The pages do not say along which axis or in which
+# byte order the four codes are packed. The reading implemented: the four codes of one
+# word belong to four consecutive 128-wide K blocks of the same row (activation scales)
+# or 128x128 block row (weight scales), the code of K block 4w + j in byte j (bits
+# 8j..8j+7) of word w; the words keep the FP32 layouts' orientation: activation scales
+# [ceil(nkb / 4)][ld] (rows contiguous), weight scales [ceil(N/128)][ceil(nkb / 4)].
+# Codes past nkb in the last word are 0.
+def ue8m0_unpack(words, nkb: int, axis: int) -> np.ndarray:
+    """Packed words (any integer dtype, 32-bit patterns) -> uint8 codes with nkb entries
+    along `axis` (the packed axis holds ceil(nkb / 4) words)."""
+    w = np.asarray(words).astype(np.int64) & 0xFFFFFFFF
+    w = np.moveaxis(w, axis, -1)
+    codes = np.stack([(w >> (8 * j)) & 0xFF for j in range(4)], axis=-1)   # [..., words, 4]
+    codes = codes.reshape(codes.shape[:-2] + (codes.shape[-2] * 4,))[..., :nkb]
+    return np.moveaxis(codes.astype(np.uint8), -1, axis)
+
+
+def ue8m0_pack(codes, axis: int) -> np.ndarray:
+    """uint8 codes -> int32 words packing four consecutive entries along `axis`."""
+    c = np.moveaxis(np.asarray(codes, dtype=np.int64), axis, -1)
+    nkb = c.shape[-1]
+    nw = (nkb + 3) // 4
+    pad = np.zeros(c.shape[:-1] + (nw * 4,), dtype=np.int64)
+    pad[..., :nkb] = c
+    pad = pad.reshape(c.shape[:-1] + (nw, 4))
+    w = pad[..., 0] | (pad[..., 1] << 8) | (pad[..., 2] << 16) | (pad[..., 3] << 24)
+    return np.moveaxis(w.astype(np.uint32).view(np.int32), -1, axis)
+
+
+def ue8m0_from_fp32(sf) -> np.ndarray:
+    """UE8M0 code of each positive, finite FP32 scale: the smallest power of two not
+    below it, 2^(code - 127) >= sf (exact for a power of two; a scale between powers
+    of two rounds up, so that no quantised value grows past the format's range)."""
+    x = np.asarray(sf, dtype=np.float32).astype(np.float64)
+    assert np.all(np.isfinite(x)) and np.all(x >= 2.0 ** -126) and np.all(x <= 2.0 ** 127), \
+        "scales must be positive normal FP32 values no larger than 2^127"
+    f, e = np.frexp(x)                   # x = f * 2^e, f in [0.5, 1)
+    k = np.where(f == 0.5, e - 1, e)     # smallest k with 2^k >= x
+    return (k + 127).astype(np.uint8)
+
+
+def transform_sf(sf, is_activation: bool, pack: bool, ld: int = None) -> np.ndarray:
+    """The scale layout the GEMMs require, from FP32 scales given per row:
+    activation scales sf [rows][nkb] -> FP32 [nkb][ld] (transposed) or, packed,
+    int32 [ceil(nkb/4)][ld]; weight scales sf [nb][nkb] -> FP32 [nb][nkb] (unchanged) or
+    int32 [nb][ceil(nkb/4)]. ld >= rows (default rows); entries past `rows` are 0."""
+    sf = np.asarray(sf, dtype=np.float32)
+    rows, nkb = sf.shape
+    if is_activation:
+        ld = rows if ld is None else ld
+        out_t = ue8m0_pack(ue8m0_from_fp32(sf), axis=1).T if pack else sf.T
+        out = np.zeros((out_t.shape[0], ld), dtype=out_t.dtype)
+        out[:, :rows] = out_t
+        return out
+    return ue8m0_pack(ue8m0_from_fp32(sf), axis=1) if pack else sf.copy()
+
+
+def gemm_nt_ue8m0_packed(A, sa_words, B, sb_words, K: int):
+    """Dense NT GEMM with packed UE8M0 scales: sa_words [ceil(nkb/4)][>=M] and sb_words
+    [ceil(N/128)][ceil(nkb/4)] (nkb = K / 128), the definition of gemm_nt_ue8m0 on the
+    unpacked codes."""
+    nkb = K // BLOCK
+    return gemm_nt_ue8m0(A, ue8m0_unpack(sa_words, nkb, axis=0), B, ue8m0_unpack(sb_words, nkb, axis=1))
+
+
 # ------------------------------------------------------------------ D = C + A B^T
 # The pages name the GEMMs D = C + A @ B (fp8_gemm_nt computes D = C + A @ B.T; es.news.
 # hada.io/topic?id=19459, "Interfaz GEMM y restricciones de layout"). With a BF16 D the
