@@ -175,6 +175,58 @@ int fp8_gemm_nt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The three NT calls with packed UE8M0 scale factors: the pages' newer API takes UE8M0
+ * scales packed four to a 32-bit int (es.news.hada.io/topic?id=19459, "Interfaz GEMM y
+ * restricciones de layout"). Same operations, shapes, preconditions and errors as
+ * fp8_gemm_nt_ue8m0 and the grouped *_ue8m0 calls; only the scale layouts differ (the
+ * pages give no axis or byte order; the reading implemented):
+ *   sa int32 [ceil(K/512)][ld_sa] (masked: [G][ceil(K/512)][ld_sa]): word w of row m
+ *      holds the E8M0 codes of row m's K blocks 4w, 4w+1, 4w+2, 4w+3 in bytes 0..3
+ *      (bits 8j..8j+7); ld_sa >= rows, ld_sa % 4 == 0, 4-byte aligned.
+ *   sb int32 [ceil(N/128)][ceil(K/512)] (grouped: [G][ceil(N/128)][ceil(K/512)]), the
+ *      same packing of each 128x128 block row's codes.
+ * Each scale is 2^(code - 127); codes 1..254 (0 and 255 are outside the contract).
+ * Bytes of the last word past K/128 are not read. fp8_transform_sf_into_required_layout
+ * produces both layouts from FP32 scales.
+ */
+int fp8_gemm_nt_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                             const void* B, int64_t ldb, const int32_t* sb,
+                             void* D, int64_t ldd, int M, int N, int K,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fp8_grouped_gemm_nt_contiguous_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                                                const void* B, int64_t ldb, const int32_t* sb,
+                                                void* D, int64_t ldd, const int32_t* m_indices,
+                                                int M_total, int N, int K, int G,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fp8_grouped_gemm_nt_masked_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                                            const void* B, int64_t ldb, const int32_t* sb,
+                                            void* D, int64_t ldd, const int32_t* masked_m,
+                                            int G, int M_max, int N, int K, int expected_m,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Scale factors into the layout the GEMMs read: the analog of the pages'
+ * transform_sf_into_required_layout (es.news.hada.io/topic?id=19459, "Utilidades y
+ * variables de entorno"; the LHS scales must be aligned and transposed, "Interfaz GEMM y
+ * restricciones de layout"). Input: FP32 scales given per row, sf[r][kb] (row stride
+ * ld_sf >= nkb), as a quantiser produces them: rows = M for activation scales (one per
+ * row per 128-wide K block), rows = ceil(N/128) for weight scales (one per 128x128
+ * block). Output (out, row stride ld_out, in 32-bit entries):
+ *   is_activation, !pack: FP32 [nkb][ld_out], out[kb][r] = sf[r][kb] (ld_out >= rows, % 4 == 0)
+ *   is_activation,  pack: int32 [ceil(nkb/4)][ld_out], packed UE8M0 words as above
+ *   !is_activation, !pack: FP32 [rows][ld_out], a copy (ld_out >= nkb)
+ *   !is_activation,  pack: int32 [rows][ld_out] packed words (ld_out >= ceil(nkb/4))
+ * Packing takes the UE8M0 code of each scale: the smallest power of two not below it
+ * (exact for powers of two; other values round up). Precondition (device data): every
+ * scale is a positive normal FP32 value of at most 2^127. Entries of out beyond the
+ * rows x columns written are untouched. Device pointers owned by the caller; the work
+ * is enqueued on `stream`. Errors: FP8GEMM_ERR_NULL, _SHAPE (rows < 0, nkb <= 0),
+ * _LAYOUT (strides, 4-byte alignment), _DEVICE, _LAUNCH; rows == 0 is a no-op.
+ */
+int fp8_transform_sf_into_required_layout(const float* sf, int64_t ld_sf, int rows, int nkb, int is_activation,
+                                          int pack, void* out, int64_t ld_out, hipStream_t stream);
+
+/*
  * M-grouped contiguous GEMM (MoE training forward / inference prefill; pages:
  * es.news.hada.io/topic?id=19459 "Dense y Grouped GEMM", contiguous layout).
  * The tokens of all G experts are concatenated along M; each expert segment is

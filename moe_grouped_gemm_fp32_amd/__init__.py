@@ -81,6 +81,12 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_gemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT, _INT]),
     "fp8_gemm_nt_noalloc": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_nt_ue8m0_packed": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_contiguous_ue8m0_packed": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_grouped_gemm_nt_masked_ue8m0_packed": (
+        _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_transform_sf_into_required_layout": (_INT, [_P, _I64, _INT, _INT, _INT, _INT, _P, _I64, _P]),
     "fp8_gemm_noalloc_scratch_bytes": (_SZ, []),
     "fp8_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P]),
     "fp8_swiglu_quantize_1x128": (_INT, [_P, _I64, _INT, _P, _P, _I64, _P, _I64, _INT, _INT, _P]),
@@ -182,16 +188,16 @@ def fp8_gemm_nt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Te
     M, K = A.shape
     N = B.shape[0]
     _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
-    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and _ld(sa) >= M, "sa must be [K/128, >=M]")
     _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
     wp, wb = _ws(workspace)
     if C is not None:
         _check_c(C, D)
-        st = lib().fp8_gemm_nt_c(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        st = lib().fp8_gemm_nt_c(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                                  _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
         _check(st, "fp8_gemm_nt_c")
         return D
-    st = lib().fp8_gemm_nt(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+    st = lib().fp8_gemm_nt(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                            _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt")
     return D
@@ -206,9 +212,9 @@ def fp8_gemm_nt_noalloc(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: 
     M, K = A.shape
     N = B.shape[0]
     _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
-    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and _ld(sa) >= M, "sa must be [K/128, >=M]")
     _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
-    st = lib().fp8_gemm_nt_noalloc(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+    st = lib().fp8_gemm_nt_noalloc(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                                    _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
     _check(st, "fp8_gemm_nt_noalloc")
     return D
@@ -226,13 +232,125 @@ def fp8_gemm_nt_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: to
     M, K = A.shape
     N = B.shape[0]
     _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
-    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= M, "sa must be [K/128, >=M]")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and _ld(sa) >= M, "sa must be [K/128, >=M]")
     _require(tuple(sb.shape) == ((N + 127) // 128, K // 128), "sb must be [ceil(N/128), K/128]")
     wp, wb = _ws(workspace)
-    st = lib().fp8_gemm_nt_ue8m0(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+    st = lib().fp8_gemm_nt_ue8m0(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                                  _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, "fp8_gemm_nt_ue8m0")
     return D
+
+
+def _ld(t: torch.Tensor, dim: int = 0) -> int:
+    """Row stride of `t` along `dim` in elements; a dimension of size 1 may carry any stride,
+    so then the rows' length (the product of the later sizes) is taken."""
+    if t.shape[dim] > 1:
+        return t.stride(dim)
+    n = 1
+    for d in t.shape[dim + 1:]:
+        n *= d
+    return n
+
+
+def _packed_common(A, sa, B, sb, D):
+    A, B = _bytes_view(A), _bytes_view(B)
+    dev = D.device
+    _require(dev.type == "cuda", "tensors must live on a GPU")
+    for name, t in (("A", A), ("sa", sa), ("B", B), ("sb", sb), ("D", D)):
+        _require(t.device == dev, f"{name} is on {t.device}, D on {dev}")
+        _require(t.stride(-1) == 1, f"{name} must have a unit inner stride")
+    _require(sa.dtype == torch.int32 and sb.dtype == torch.int32, "packed UE8M0 scales must be int32 words")
+    _require(D.dtype == torch.bfloat16, "D must be bfloat16")
+    _require(sb.is_contiguous(), "sb must be contiguous")
+    return A, B, dev
+
+
+def fp8_gemm_nt_ue8m0_packed(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp8_gemm_nt with packed UE8M0 scales: sa int32 [ceil(K/512), ld_sa >= M] (word w of
+    row m holds the codes of K blocks 4w..4w+3 in bytes 0..3), sb int32 [ceil(N/128),
+    ceil(K/512)] (see transform_sf_into_required_layout)."""
+    A, B, dev = _packed_common(A, sa, B, sb, D)
+    M, K = A.shape
+    N = B.shape[0]
+    nkw = (K // 128 + 3) // 4
+    _require(B.shape[1] == K and tuple(D.shape) == (M, N), "shape mismatch")
+    _require(sa.dim() == 2 and sa.shape[0] == nkw and _ld(sa) >= M, "sa must be [ceil(K/512), >=M]")
+    _require(tuple(sb.shape) == ((N + 127) // 128, nkw), "sb must be [ceil(N/128), ceil(K/512)]")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_gemm_nt_ue8m0_packed(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0),
+                                        _ptr(sb), _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
+    _check(st, "fp8_gemm_nt_ue8m0_packed")
+    return D
+
+
+def fp8_grouped_gemm_nt_contiguous_ue8m0_packed(A, sa, B, sb, D, m_indices, workspace=None, stream=None):
+    """The contiguous grouped GEMM with packed UE8M0 scales: sa int32 [ceil(K/512),
+    >=M_total], sb int32 [G, ceil(N/128), ceil(K/512)]."""
+    A, B, dev = _packed_common(A, sa, B, sb, D)
+    Mt, K = A.shape
+    G, N, K2 = B.shape
+    nkw = (K // 128 + 3) // 4
+    _require(K2 == K and tuple(D.shape) == (Mt, N) and B.is_contiguous(), "shape mismatch")
+    _require(sa.dim() == 2 and sa.shape[0] == nkw and _ld(sa) >= Mt, "sa must be [ceil(K/512), >=M_total]")
+    _require(tuple(sb.shape) == (G, (N + 127) // 128, nkw), "sb must be [G, ceil(N/128), ceil(K/512)]")
+    _require(m_indices.dtype == torch.int32 and m_indices.numel() == Mt and m_indices.device == dev
+             and m_indices.is_contiguous(), "m_indices must be a contiguous int32 [M_total] device tensor")
+    wp, wb = _ws(workspace)
+    st = lib().fp8_grouped_gemm_nt_contiguous_ue8m0_packed(
+        _ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
+        _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
+    _check(st, "fp8_grouped_gemm_nt_contiguous_ue8m0_packed")
+    return D
+
+
+def fp8_grouped_gemm_nt_masked_ue8m0_packed(A, sa, B, sb, D, masked_m, expected_m: int, stream=None):
+    """The masked grouped GEMM with packed UE8M0 scales: sa int32 [G, ceil(K/512),
+    >=M_max], sb int32 [G, ceil(N/128), ceil(K/512)]."""
+    A, B, dev = _packed_common(A, sa, B, sb, D)
+    G, M_max, K = A.shape
+    G2, N, K2 = B.shape
+    nkw = (K // 128 + 3) // 4
+    _require(G2 == G and K2 == K and tuple(D.shape) == (G, M_max, N), "shape mismatch")
+    for name, t in (("A", A), ("B", B), ("D", D), ("sa", sa)):
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(sa.dim() == 3 and sa.shape[0] == G and sa.shape[1] == nkw and sa.shape[2] >= M_max,
+             "sa must be [G, ceil(K/512), >=M_max]")
+    _require(tuple(sb.shape) == (G, (N + 127) // 128, nkw), "sb must be [G, ceil(N/128), ceil(K/512)]")
+    _require(masked_m.dtype == torch.int32 and masked_m.numel() == G and masked_m.device == dev
+             and masked_m.is_contiguous(), "masked_m must be a contiguous int32 [G] device tensor")
+    st = lib().fp8_grouped_gemm_nt_masked_ue8m0_packed(
+        _ptr(A), A.stride(1), _ptr(sa), _ld(sa, 1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
+        _ptr(masked_m), G, M_max, N, K, int(expected_m), None, 0, _stream(dev, stream))
+    _check(st, "fp8_grouped_gemm_nt_masked_ue8m0_packed")
+    return D
+
+
+def transform_sf_into_required_layout(sf: torch.Tensor, is_activation: bool, pack: bool, ld: Optional[int] = None,
+                                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """FP32 scale factors given per row, sf [rows, nkb] (activation: rows = M; weight:
+    rows = ceil(N/128)), into the layout the GEMMs read, computed by
+    fp8_transform_sf_into_required_layout: activation -> [nkb, ld] FP32 or [ceil(nkb/4),
+    ld] int32 packed UE8M0 (ld >= rows, default scale_ld(rows)); weight -> [rows, nkb]
+    FP32 or [rows, ceil(nkb/4)] int32 packed."""
+    _require(sf.device.type == "cuda" and sf.dtype == torch.float32 and sf.dim() == 2 and sf.stride(-1) == 1,
+             "sf must be a 2-D float32 GPU tensor with unit inner stride")
+    rows, nkb = sf.shape
+    cols = (nkb + 3) // 4 if pack else nkb
+    dt = torch.int32 if pack else torch.float32
+    if out is None:
+        if is_activation:
+            out = torch.zeros(cols, scale_ld(rows) if ld is None else ld, dtype=dt, device=sf.device)
+        else:
+            out = torch.zeros(rows, cols, dtype=dt, device=sf.device)
+    _require(out.dtype == dt and out.dim() == 2 and out.stride(-1) == 1 and out.device == sf.device,
+             "out has the wrong type or layout")
+    _require(out.shape[0] == (cols if is_activation else rows), "out has the wrong number of rows")
+    st = lib().fp8_transform_sf_into_required_layout(_ptr(sf), sf.stride(0), rows, nkb, int(bool(is_activation)),
+                                                     int(bool(pack)), _ptr(out), out.stride(0),
+                                                     _stream(sf.device, stream))
+    _check(st, "fp8_transform_sf_into_required_layout")
+    return out
 
 
 QUANT_BF16, QUANT_FP32 = 0, 1  # fp8_quantize_1x128 input types
@@ -255,10 +373,10 @@ def quantize_1x128(X: torch.Tensor, Q: Optional[torch.Tensor] = None, sa: Option
         sa = torch.empty(K // 128, scale_ld(M), dtype=torch.float32, device=X.device)
     Q = _bytes_view(Q)
     _require(tuple(Q.shape) == (M, K) and Q.stride(-1) == 1 and Q.device == X.device, "Q must be [M, K]")
-    _require(sa.dtype == torch.float32 and sa.shape[0] == K // 128 and sa.stride(-1) == 1 and sa.stride(0) >= M,
+    _require(sa.dtype == torch.float32 and sa.shape[0] == K // 128 and sa.stride(-1) == 1 and _ld(sa) >= M,
              "sa must be float32 [K/128, >=M]")
     st = lib().fp8_quantize_1x128(_ptr(X), X.stride(0), QUANT_BF16 if X.dtype == torch.bfloat16 else QUANT_FP32,
-                                  _ptr(Q), Q.stride(0), _ptr(sa), sa.stride(0), M, K, _stream(X.device, stream))
+                                  _ptr(Q), Q.stride(0), _ptr(sa), _ld(sa), M, K, _stream(X.device, stream))
     _check(st, "fp8_quantize_1x128")
     return Q, sa
 
@@ -280,13 +398,13 @@ def swiglu_quantize_1x128(H: torch.Tensor, m_indices: Optional[torch.Tensor] = N
         sa = torch.empty(F // 128, scale_ld(M), dtype=torch.float32, device=H.device)
     Q = _bytes_view(Q)
     _require(tuple(Q.shape) == (M, F) and Q.stride(-1) == 1 and Q.device == H.device, "Q must be [M, F]")
-    _require(sa.dtype == torch.float32 and sa.shape[0] == F // 128 and sa.stride(-1) == 1 and sa.stride(0) >= M,
+    _require(sa.dtype == torch.float32 and sa.shape[0] == F // 128 and sa.stride(-1) == 1 and _ld(sa) >= M,
              "sa must be float32 [F/128, >=M]")
     if m_indices is not None:
         _require(m_indices.dtype == torch.int32 and m_indices.numel() >= M and m_indices.device == H.device,
                  "m_indices must be int32 [>=M] on H's device")
     st = lib().fp8_swiglu_quantize_1x128(_ptr(H), H.stride(0), QUANT_BF16 if H.dtype == torch.bfloat16 else QUANT_FP32,
-                                         _ptr(m_indices), _ptr(Q), Q.stride(0), _ptr(sa), sa.stride(0), M, F,
+                                         _ptr(m_indices), _ptr(Q), Q.stride(0), _ptr(sa), _ld(sa), M, F,
                                          _stream(H.device, stream))
     _check(st, "fp8_swiglu_quantize_1x128")
     return Q, sa
@@ -305,7 +423,7 @@ def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, s
     G, N, K2 = B.shape
     _require(K2 == K and tuple(D.shape) == (Mt, N), "shape mismatch")
     _require(B.is_contiguous(), "B must be contiguous [G, N, K]")
-    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and sa.stride(0) >= Mt, "sa must be [K/128, >=M_total]")
+    _require(sa.dim() == 2 and sa.shape[0] == K // 128 and _ld(sa) >= Mt, "sa must be [K/128, >=M_total]")
     _require(tuple(sb.shape) == (G, (N + 127) // 128, K // 128), "sb must be [G, ceil(N/128), K/128]")
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == Mt and m_indices.device == dev
              and m_indices.is_contiguous(), "m_indices must be a contiguous int32 [M_total] device tensor")
@@ -314,13 +432,13 @@ def fp8_grouped_gemm_nt_contiguous(A, sa, B, sb, D, m_indices, workspace=None, s
         _require(not ue8m0, "C is supported with FP32 scales")
         _check_c(C, D)
         st = lib().fp8_grouped_gemm_nt_contiguous_c(
-            _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(0),
+            _ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(0),
             _ptr(D), D.stride(0), _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
         _check(st, "fp8_grouped_gemm_nt_contiguous_c")
         return D
     name = "fp8_grouped_gemm_nt_contiguous_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_contiguous"
     st = getattr(lib(), name)(
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
+        _ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(0),
         _ptr(m_indices), Mt, N, K, G, wp, wb, _stream(dev, stream))
     _check(st, name)
     return D
@@ -353,13 +471,13 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
         _check_c(C, D)
         _require(C.is_contiguous(), "C must be contiguous")
         st = lib().fp8_grouped_gemm_nt_masked_c(
-            _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(1),
+            _ptr(A), A.stride(1), _ptr(sa), _ld(sa, 1), _ptr(B), B.stride(1), _ptr(sb), _ptr(C), C.stride(1),
             _ptr(D), D.stride(1), _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
         _check(st, "fp8_grouped_gemm_nt_masked_c")
         return D
     name = "fp8_grouped_gemm_nt_masked_ue8m0" if ue8m0 else "fp8_grouped_gemm_nt_masked"
     st = getattr(lib(), name)(
-        _ptr(A), A.stride(1), _ptr(sa), sa.stride(1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
+        _ptr(A), A.stride(1), _ptr(sa), _ld(sa, 1), _ptr(B), B.stride(1), _ptr(sb), _ptr(D), D.stride(1),
         _ptr(masked_m), G, M_max, N, K, int(expected_m), wp, wb, _stream(dev, stream))
     _check(st, name)
     return D
@@ -384,10 +502,10 @@ def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream, C=None):
     if C is not None:
         _check_c(C, D)
         name = name + "_c"
-        st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                                   _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
     else:
-        st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
                                   _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
     _check(st, name)
     return D
@@ -447,7 +565,7 @@ def k_grouped_fp8_gemm_tn_contiguous(A, sa, B, sb, D, ks, accumulate: bool = Fal
     ks_arr = (ctypes.c_int32 * max(G, 1))(*ks)
     name = "fp8_k_grouped_gemm_tn_contiguous_ue8m0" if ue8m0 else "fp8_k_grouped_gemm_tn_contiguous"
     st = getattr(lib(), name)(
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb), sb.stride(0),
+        _ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb), sb.stride(0),
         _ptr(D), D.stride(1), D.stride(0), ctypes.cast(ks_arr, ctypes.c_void_p), G, M, N, int(bool(accumulate)),
         _stream(dev, stream))
     _check(st, name)

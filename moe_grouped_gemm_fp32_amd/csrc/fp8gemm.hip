@@ -371,6 +371,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.split_k = pl.split;
   p.kb_per_split = pl.kbps;
   p.num_kb = K / fp8gemm::kBlockK;
+  p.sb_kstride = p.sf_packed ? (p.num_kb + 3) / 4 : p.num_kb;
   p.num_units = (int)pl.units;
   p.full_tiles = (int)pl.full;
   p.group_m = 8;
@@ -401,10 +402,17 @@ Params base_params(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
   return p;
 }
 
+// Scale entries per 128-row weight block per group: K/128 FP32 values, or ceil(K/512)
+// packed UE8M0 words.
+int64_t scale_kstride(int K, bool packed) {
+  const int nkb = K / fp8gemm::kBlockK;
+  return packed ? (nkb + 3) / 4 : nkb;
+}
+
 int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                        const float* sb, void* D, int64_t ldd, const int32_t* m_indices, int M_total, int N, int K,
                        int G, void* workspace, size_t workspace_bytes, hipStream_t stream, bool e8,
-                       const void* C = nullptr, int64_t ldc = 0) {
+                       const void* C = nullptr, int64_t ldc = 0, bool packed = false) {
   int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_total, N, K);
   if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
   if (st != FP8GEMM_OK) return st;
@@ -417,16 +425,19 @@ int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_s
   p.C = static_cast<const uint16_t*>(C);
   p.ldc = ldc;
   p.b_gstride = (int64_t)N * ldb;
-  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  p.sf_packed = packed ? 1 : 0;
+  p.sb_gstride = ceil_div(N, 128) * scale_kstride(K, packed);
   // tiles must not straddle two 128-row expert blocks
   if (g_forced && 128 % g_forced_cfg.block_m != 0) return FP8GEMM_ERR_CONFIG;
-  return run(FP8GEMM_KIND_CONTIGUOUS, e8 ? "contiguous ue8m0" : "contiguous", p, M_total, N, K, G, 0, workspace,
+  return run(FP8GEMM_KIND_CONTIGUOUS, e8 ? (packed ? "contiguous ue8m0 packed" : "contiguous ue8m0") : "contiguous",
+             p, M_total, N, K, G, 0, workspace,
              workspace_bytes, stream, e8);
 }
 
 int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                    const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G, int M_max, int N, int K,
-                   int expected_m, hipStream_t stream, bool e8, const void* C = nullptr, int64_t ldc = 0) {
+                   int expected_m, hipStream_t stream, bool e8, const void* C = nullptr, int64_t ldc = 0,
+                   bool packed = false) {
   int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
   if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
   if (st != FP8GEMM_OK) return st;
@@ -437,15 +448,16 @@ int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
   p.M = M_max;
   p.masked_m = masked_m;
   p.a_gstride = (int64_t)M_max * lda;
-  p.sa_gstride = (int64_t)(K / 128) * ld_sa;
+  p.sf_packed = packed ? 1 : 0;
+  p.sa_gstride = scale_kstride(K, packed) * ld_sa;
   p.b_gstride = (int64_t)N * ldb;
-  p.sb_gstride = ceil_div(N, 128) * (K / 128);
+  p.sb_gstride = ceil_div(N, 128) * scale_kstride(K, packed);
   p.d_gstride = (int64_t)M_max * ldd;
   p.C = static_cast<const uint16_t*>(C);
   p.ldc = ldc;
   p.c_gstride = (int64_t)M_max * ldc;
-  return run(FP8GEMM_KIND_MASKED, e8 ? "masked ue8m0" : "masked", p, M_max, N, K, G, expected_m, nullptr, 0, stream,
-             e8);
+  return run(FP8GEMM_KIND_MASKED, e8 ? (packed ? "masked ue8m0 packed" : "masked ue8m0") : "masked", p, M_max, N,
+             K, G, expected_m, nullptr, 0, stream, e8);
 }
 
 }  // namespace
@@ -506,6 +518,39 @@ int fp8_gemm_nt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa
   Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
   p.M = M;
   return run(FP8GEMM_KIND_DENSE, "dense ue8m0", p, M, N, K, 1, 0, workspace, workspace_bytes, stream, true);
+}
+
+int fp8_gemm_nt_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa, const void* B, int64_t ldb,
+                             const int32_t* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const float* saf = reinterpret_cast<const float*>(sa);
+  const float* sbf = reinterpret_cast<const float*>(sb);
+  const int st = check_common(A, lda, saf, ld_sa, B, ldb, sbf, D, ldd, M, N, K);
+  if (st != FP8GEMM_OK) return st;
+  if (M == 0) return FP8GEMM_OK;
+  Params p = base_params(A, lda, saf, ld_sa, B, ldb, sbf, D, ldd);
+  p.M = M;
+  p.sf_packed = 1;
+  return run(FP8GEMM_KIND_DENSE, "dense ue8m0 packed", p, M, N, K, 1, 0, workspace, workspace_bytes, stream, true);
+}
+
+int fp8_grouped_gemm_nt_contiguous_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                                                const void* B, int64_t ldb, const int32_t* sb, void* D, int64_t ldd,
+                                                const int32_t* m_indices, int M_total, int N, int K, int G,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return grouped_contiguous(A, lda, reinterpret_cast<const float*>(sa), ld_sa, B, ldb,
+                            reinterpret_cast<const float*>(sb), D, ldd, m_indices, M_total, N, K, G, workspace,
+                            workspace_bytes, stream, true, nullptr, 0, true);
+}
+
+int fp8_grouped_gemm_nt_masked_ue8m0_packed(const void* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                                            const void* B, int64_t ldb, const int32_t* sb, void* D, int64_t ldd,
+                                            const int32_t* masked_m, int G, int M_max, int N, int K, int expected_m,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return grouped_masked(A, lda, reinterpret_cast<const float*>(sa), ld_sa, B, ldb, reinterpret_cast<const float*>(sb),
+                        D, ldd, masked_m, G, M_max, N, K, expected_m, stream, true, nullptr, 0, true);
 }
 
 int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
@@ -810,6 +855,25 @@ int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int
     hipLaunchKernelGGL((fp8gemm::quantize_1x128_kernel<float, true>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const float*>(H), ldh, static_cast<uint8_t*>(Q), ldq, sa, ld_sa, M, nkb,
                        m_indices, F);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
+}
+
+int fp8_transform_sf_into_required_layout(const float* sf, int64_t ld_sf, int rows, int nkb, int is_activation,
+                                          int pack, void* out, int64_t ld_out, hipStream_t stream) {
+  if (!sf || !out) return FP8GEMM_ERR_NULL;
+  if (rows < 0 || nkb <= 0) return FP8GEMM_ERR_SHAPE;
+  const int64_t cols = pack ? (nkb + 3) / 4 : nkb;
+  if (ld_sf < nkb || !aligned(sf, 4) || !aligned(out, 4)) return FP8GEMM_ERR_LAYOUT;
+  if (is_activation ? (ld_out < rows || ld_out % 4 != 0) : ld_out < cols) return FP8GEMM_ERR_LAYOUT;
+  if ((int64_t)rows * cols > INT32_MAX) return FP8GEMM_ERR_SHAPE;
+  int st;
+  const int cus = effective_cus(true, &st);
+  if (st != FP8GEMM_OK) return st;
+  if (rows == 0) return FP8GEMM_OK;
+  const int64_t n = (int64_t)rows * cols;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, 256), (int64_t)cus * 8));
+  hipLaunchKernelGGL(fp8gemm::transform_sf_kernel, dim3(grid), dim3(256), 0, stream, sf, ld_sf, rows, nkb,
+                     is_activation ? 1 : 0, pack ? 1 : 0, static_cast<uint32_t*>(out), ld_out);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 

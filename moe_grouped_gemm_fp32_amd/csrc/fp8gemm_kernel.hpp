@@ -64,6 +64,9 @@ struct Params {
   const uint16_t* C;         // optional BF16 addend of D = C + A B^T (nullptr: none); may alias D
   int64_t ldc, c_gstride;    // C row stride, per-group stride (masked)
   int c_vec;                 // 1: C rows allow 16-byte loads (ldc % 8 == 0, C 16-byte aligned)
+  int sf_packed;             // E8: sa / sb hold packed UE8M0 words (the codes of K blocks 4w..4w+3
+                             // in bytes 0..3 of word w) instead of FP32 powers of two
+  int sb_kstride;            // entries per weight-scale row: K/128 (FP32) or ceil(K/512) (packed)
   float* ws;                 // split-K partials [split tile][split][BM*BN]
   int32_t* counters;         // split-K arrival counters [split tile]
 };
@@ -465,9 +468,12 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     const int kb0 = S_u > 1 ? split * p.kb_per_split : 0;
     const int nk = S_u > 1 ? min(p.num_kb, kb0 + p.kb_per_split) - kb0 : p.num_kb;
     const uint8_t* Ag = uni(p.A + (MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)kb0 * kBlockK);
-    const float* sag = uni(p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kb0 * p.ld_sa);
+    // scale rows: one per K block (FP32), or one word row per four K blocks (packed UE8M0)
+    const bool packed = E8 && p.sf_packed;
+    const int kw0 = packed ? kb0 >> 2 : kb0;
+    const float* sag = uni(p.sa + (MASKED ? (int64_t)g * p.sa_gstride : 0) + (int64_t)kw0 * p.ld_sa);
     const uint8_t* Bg = uni(p.B + (int64_t)g * p.b_gstride + (int64_t)kb0 * kBlockK);
-    const float* sbg = uni(p.sb + (int64_t)g * p.sb_gstride + kb0);
+    const float* sbg = uni(p.sb + (int64_t)g * p.sb_gstride + kw0);
 
     // ---- direct-to-LDS load plan. Load instruction r of this wave fills LDS row
     // positions 8*grp .. 8*grp+7 (1 KB) of a stage: lane l writes chunk position l & 7
@@ -502,7 +508,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     } else {
       constexpr int NB = BN >= kBlockK ? BN / kBlockK : 1;
       const int nb = min(lane, NB - 1);
-      sc_src = sbg + (int64_t)(min(n0 + nb * kBlockK, p.N - 1) / kBlockK) * p.num_kb;
+      sc_src = sbg + (int64_t)(min(n0 + nb * kBlockK, p.N - 1) / kBlockK) * p.sb_kstride;
       sc_step = 1;
     }
 
@@ -519,7 +525,8 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         else
           dma16(Bg + (int64_t)i * kBlockK, b_off[r], base + A_BYTES + (r * NW + wave) * 1024);
       } else {
-        dma4v(sc_src + i * sc_step, base + A_BYTES + B_BYTES + (wave < SA_WAVES ? wave * 256 : BM * 4));
+        dma4v(sc_src + (packed ? ((kb0 + i) >> 2) - kw0 : i) * sc_step,
+              base + A_BYTES + B_BYTES + (wave < SA_WAVES ? wave * 256 : BM * 4));
       }
     };
     auto issue = [&](int i, int stage) {
@@ -587,16 +594,20 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     // result is ready by then. Scheduling barriers keep the slots in this order so
     // the load traffic runs in the matrix unit's shadow.
     constexpr int NMF = TM * TN;
-    auto compute = [&](auto buf_c, auto&& side) {
+    // kbi: the computed stage's K block, counted from kb0 (selects a packed code's byte)
+    auto compute = [&](auto buf_c, auto&& side, int kbi) {
       constexpr int buf = decltype(buf_c)::value;
       if constexpr (E8) {
         // scale operands: the exponent byte of each power-of-two scale (the E8M0 code);
         // the first MFMA operand (B rows) takes the tile's weight scale, the second
         // (A rows) the activation scale of the lane's row
+        // (an FP32 power of two carries its code in the exponent field, bits 23..30; a
+        // packed word carries K block 4w + j's code in byte j)
+        const int sh = packed ? 8 * ((kb0 + kbi) & 3) : 23;
         int ea[TM];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) ea[t] = (__float_as_int(sa_r[buf][t]) >> 23) & 0xFF;
-        const int eb = (__float_as_int(sb_r[buf]) >> 23) & 0xFF;
+        for (int t = 0; t < TM; ++t) ea[t] = (__float_as_int(sa_r[buf][t]) >> sh) & 0xFF;
+        const int eb = (__float_as_int(sb_r[buf]) >> sh) & 0xFF;
 #pragma unroll
         for (int k = 0; k < NMF; ++k) {
           const int t = k / TN, j = k % TN;
@@ -678,7 +689,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         compute(cur_c, [&](int k) {
           if constexpr (REFILL) share(k, LPS, [&](int q) { issue_item(i + STAGES, ws, q); });
           if constexpr (MORE) share(k, NREAD, [&](int q) { read_item(rs, std::integral_constant<int, nxt>{}, q); });
-        });
+        }, i);
         wait_lgkmcnt0();
       };
       using T = std::true_type;
@@ -739,7 +750,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         if constexpr (REFILL) issue(ld, ld % STAGES);
         wait_lgkmcnt0();
       };
-      auto phase_compute = [&]() { compute(C0{}, [](int) {}); };
+      auto phase_compute = [&](int j) { compute(C0{}, [](int) {}, j); };
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue(s, s);
@@ -753,14 +764,14 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
           barrier();
           phase_read(j, j + STAGES - 1, std::true_type{});
           barrier();
-          phase_compute();
+          phase_compute(j);
         }
         for (; j < nk; ++j) {
           wait_vmcnt<0>();
           barrier();
           phase_read(j, 0, std::false_type{});
           barrier();
-          phase_compute();
+          phase_compute(j);
         }
         barrier();
       } else {
@@ -772,14 +783,14 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
           phase_read(j, j + STAGES - 1, std::true_type{});
           wait_vmcnt<LPS * (STAGES - 2)>();  // stage j + 1
           barrier();
-          phase_compute();
+          phase_compute(j);
         }
         for (; j < nk; ++j) {
           barrier();
           phase_read(j, 0, std::false_type{});
           wait_vmcnt<0>();
           barrier();
-          phase_compute();
+          phase_compute(j);
         }
       }
     }

@@ -94,4 +94,39 @@ __global__ void __launch_bounds__(256) quantize_1x128_kernel(const T* X, int64_t
   }
 }
 
+// UE8M0 code of a positive normal FP32 scale: the smallest power of two not below it,
+// i.e. the exponent field, plus one when a mantissa bit is set (exact for powers of two).
+__device__ __forceinline__ uint32_t ue8m0_code(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return ((b >> 23) & 0xFF) + ((b & 0x7FFFFFu) != 0u ? 1u : 0u);
+}
+
+// Scale factors given per row, sf[r][kb] (row stride ld_sf), into the layout the GEMMs
+// read: activation scales transposed to out[kb][r] (FP32) or out[w][r] (packed UE8M0
+// words, K blocks 4w..4w+3 in bytes 0..3), weight scales kept as out[r][kb] (FP32) or
+// packed to out[r][w]; out's row stride is ld_out. One 32-bit output per thread (grid-
+// stride); for activation scales consecutive threads write consecutive rows, the
+// output's contiguous axis.
+__global__ void transform_sf_kernel(const float* __restrict__ sf, int64_t ld_sf, int rows, int nkb,
+                                    int is_activation, int pack, uint32_t* __restrict__ out, int64_t ld_out) {
+  const int cols = pack ? (nkb + 3) / 4 : nkb;
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int r = is_activation ? (int)(idx % rows) : (int)(idx / cols);
+    const int c = is_activation ? (int)(idx / rows) : (int)(idx % cols);
+    const float* src = sf + (int64_t)r * ld_sf;
+    uint32_t v = 0;
+    if (pack) {
+      for (int j = 0; j < 4; ++j)
+        if (4 * c + j < nkb) v |= ue8m0_code(src[4 * c + j]) << (8 * j);
+    } else {
+      v = __float_as_uint(src[c]);
+    }
+    if (is_activation)
+      out[(int64_t)c * ld_out + r] = v;
+    else
+      out[(int64_t)r * ld_out + c] = v;
+  }
+}
+
 }  // namespace fp8gemm

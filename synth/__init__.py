@@ -109,6 +109,23 @@ def quantize_weight(w: torch.Tensor, pow2: bool = False):
     return q.contiguous(), scale.contiguous()
 
 
+def pack_ue8m0(scales: torch.Tensor, axis: int) -> torch.Tensor:
+    """Power-of-two FP32 scales -> int32 words of packed E8M0 codes (a power of two's code
+    is its FP32 exponent field): entries 4w..4w+3 along `axis` in bytes 0..3 of word w,
+    the last word zero-padded. The packed-UE8M0 inputs of the *_ue8m0_packed calls."""
+    codes = ((scales.contiguous().view(torch.int32) >> 23) & 0xFF).to(torch.int64).movedim(axis, -1)
+    n = codes.shape[-1]
+    nw = (n + 3) // 4
+    pad = torch.zeros(codes.shape[:-1] + (nw * 4,), dtype=torch.int64, device=codes.device)
+    pad[..., :n] = codes
+    pad = pad.reshape(codes.shape[:-1] + (nw, 4))
+    w = pad[..., 0] | (pad[..., 1] << 8) | (pad[..., 2] << 16) | (pad[..., 3] << 24)
+    w = torch.where(w >= 2 ** 31, w - 2 ** 32, w).to(torch.int32).movedim(-1, axis)
+    out = torch.empty(w.shape, dtype=torch.int32, device=w.device)  # row-major strides
+    out.copy_(w)
+    return out
+
+
 def random_bytes(shape, gen: torch.Generator, device) -> torch.Tensor:
     """Uniform random bytes (NaN codes 0x7F/0xFF included): content of dead rows."""
     return torch.randint(0, 256, tuple(shape), generator=gen, device=device, dtype=torch.uint8)

@@ -293,3 +293,31 @@ def test_every_declaration_cites_its_passage():
     missing = [n for n, c in flat if not (PAGE_CITATION.search(c) or "no counterpart on the pages" in c
                                            or "cannot allocate" in c)]
     assert not missing, "declarations without a citation: %s" % missing
+
+
+def test_packed_and_transform_argument_validation_without_launch():
+    L = fg.lib()
+
+    def dense(**kw):
+        a = dict(A=1 << 20, lda=512, sa=1 << 20, ld_sa=64, B=1 << 20, ldb=512, sb=1 << 20, D=1 << 20, ldd=256,
+                 M=64, N=256, K=512)
+        a.update(kw)
+        mk = lambda v: P(v) if v else None
+        return L.fp8_gemm_nt_ue8m0_packed(mk(a["A"]), a["lda"], mk(a["sa"]), a["ld_sa"], mk(a["B"]), a["ldb"],
+                                          mk(a["sb"]), mk(a["D"]), a["ldd"], a["M"], a["N"], a["K"], None, 0, None)
+    assert dense(sa=0) == -1 and dense(K=100) == -2 and dense(ld_sa=62) == -3 and dense(M=0) == 0
+
+    def tr(**kw):
+        a = dict(sf=1 << 20, ld_sf=9, rows=300, nkb=9, act=1, pack=1, out=1 << 20, ld_out=300)
+        a.update(kw)
+        mk = lambda v: P(v) if v else None
+        return L.fp8_transform_sf_into_required_layout(mk(a["sf"]), a["ld_sf"], a["rows"], a["nkb"], a["act"],
+                                                       a["pack"], mk(a["out"]), a["ld_out"], None)
+    assert tr(sf=0) == -1 and tr(out=0) == -1
+    assert tr(nkb=0) == -2 and tr(rows=-1) == -2
+    assert tr(ld_sf=8) == -3 and tr(ld_out=299) == -3 and tr(ld_out=302) == -3   # < rows; not a multiple of 4
+    assert tr(act=0, ld_out=2) == -3 and tr(act=0, pack=0, ld_out=8) == -3      # < ceil(nkb/4); < nkb
+    assert tr(sf=(1 << 20) + 2) == -3
+    import torch
+    if not torch.cuda.is_available():
+        assert tr() == -5 and tr(act=0, ld_out=3) == -5
