@@ -1,16 +1,22 @@
 """Benchmark of the FP8 block-scaled NT GEMM on one MI355X.
 
 One step = one pass over the dense DeepSeek-V3-like shape list (M in {64, 128, 4096}
-x (N, K) in {(2112,7168), (24576,1536), (32768,512), (7168,16384), (4096,7168),
+x (N,K) in {(2112,7168), (24576,1536), (32768,512), (7168,16384), (4096,7168),
 (7168,2048)}), A ~ N(0,1) and B ~ N(0,0.02) quantised to e4m3 with 1x128 / 128x128
 FP32 scales, BF16 output. Every shape has its own resident operands (no operand is
 reused within a step, so each GEMM streams its inputs from HBM). Prints one JSON line.
 
   value     = total algorithmic FP8 FLOPs of a step / measured step time (TFLOP/s)
   per_shape = per-GEMM kernel time from HIP events on the launch stream, FP8 TFLOP/s,
-              HBM GB/s of the algorithmic bytes, and the fraction of the binding roofline
-  roofline  = the same for the shape that takes the most time
-  cpu_baseline = the CPU oracle timed on one full shape on this host
+              HBM GB/s of the algorithmic bytes, and the fraction of the binding roofline:
+              the 18 dense shapes (the step), then, timed separately, the small dense
+              128x256x512 case (per-call latency, no roofline fraction), the two
+              contiguous grouped cases, the ten masked decode cases and the MoE FFN pair
+  roofline  = the same for the shape that takes the most time, its mean launch time from
+              HIP events on the launch stream (avg_us), traffic from the rocprofv3 counter
+              table of the same kernel sources (null when the sources have changed)
+  cpu_baseline = the CPU oracle timed on one full shape on this host (median of 3) and
+              single-threaded on the small case
 """
 import argparse
 import csv
@@ -235,36 +241,40 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline():
-    """The CPU oracle (as it stands) on the full M=4096, N=7168, K=16384 dense shape (the
-    benchmark's dominant shape; ~10 s on a 16-thread host)."""
+def cpu_baseline(runs=3):
+    """The CPU oracle, as it stands, on the full M=4096, N=7168, K=16384 dense shape (the
+    dominant shape of the timed step; ~8 s per run on a 16-thread host): median of `runs`
+    runs on the host's cores, plus the median of three single-thread runs of the small
+    128x256x512 case."""
     import numpy as np
-    import torch
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-    except Exception:  # pragma: no cover
-        threadpool_info = None
+    from threadpoolctl import threadpool_limits
     M, N, K = 4096, 7168, 16384
     c = synth.dense_case(M, N, K, seed=99, device="cpu")
     args = [c[k].numpy() for k in ("A", "sa", "B", "sb")]
-    t0 = time.perf_counter()
-    oracle.gemm_nt(*args)
-    dt = time.perf_counter() - t0
-    threads = None
-    if threadpool_info is not None:
-        info = threadpool_info()
-        blas = [i for i in info if i.get("user_api") == "blas"]
-        if blas:
-            threads = int(blas[0].get("num_threads"))
-    if threads is None:
-        threads = len(os.sched_getaffinity(0))
-    del torch
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.gemm_nt(*args)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    threads = blas_threads()
+    small = synth.dense_case(128, 256, 512, seed=98, device="cpu")
+    sargs = [small[k].numpy() for k in ("A", "sa", "B", "sb")]
+    st = []
+    with threadpool_limits(limits=1):
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.gemm_nt(*sargs)
+            st.append(time.perf_counter() - t0)
+    sdt = float(np.median(st))
     return {"value": round(2.0 * M * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "runs_seconds": [round(t, 3) for t in times],
             "sample": "full oracle (e4m3 decode, per-128-K FP64 block matmul, scaling, BF16 RNE) of the "
-                      "dense M=4096 N=7168 K=16384 shape, 962 GFLOP"}
+                      "dense M=4096 N=7168 K=16384 shape, 962 GFLOP, median of %d runs" % runs,
+            "single_thread_small": {"shape": "128x256x512", "seconds": round(sdt, 5),
+                                    "tflops": round(2.0 * 128 * 256 * 512 / sdt / 1e12, 6), "cores": 1}}
 
 
 def grouped_work(m_live, g_active, N, K, m_padded=None):
@@ -278,45 +288,86 @@ def grouped_work(m_live, g_active, N, K, m_padded=None):
     return flops, nbytes, padded
 
 
-def grouped_bench(args):
-    """--workload grouped: the M-grouped configurations (contiguous C3, masked decode C4,
-    the MoE FFN pair C5), one step = every case once, per-case times from HIP events on
-    the launch stream. Prints one JSON line (not the default benchmark)."""
+def time_cases(fns, steps, warmup):
+    """Run every callable once per step: `warmup` untimed steps, then `steps` timed steps
+    (wall time, bracketed by synchronisations), then per-call durations from HIP events on
+    the launch stream over `steps` more steps (one untimed step first and a single
+    synchronisation at the end, so the host stays ahead of the GPU and no event pair
+    includes host launch latency). Returns (ms per step, [mean ms per call])."""
+    import torch
+
+    def step(events=None):
+        for i, fn in enumerate(fns):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / steps * 1e3
+    step()
+    all_ev = []
+    for _ in range(steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+        step(ev)
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    per = [0.0] * len(fns)
+    for ev in all_ev:
+        for i, (a, b) in enumerate(ev):
+            per[i] += a.elapsed_time(b)
+    return ms_per_step, [v / steps for v in per]
+
+
+def grouped_cases(dev, ue=False):
+    """The M-grouped workloads with their resident operands: contiguous (4 experts x 8192
+    rows, N=4096, K=7168; 8 experts x 4096 rows, N=7168, K=2048), masked decode (G in 1, 2,
+    4, 8, 16 at (N, K) = (4096, 7168) and (7168, 2048), M_max 4096, masked_m uniform in
+    [179, 333], expected_m 256) and the MoE FFN pair (4096 tokens, 256 experts, top-8
+    Zipf(1.1) routing, padded to 128 rows per expert; the down GEMM's input is the SwiGLU
+    of the gate+up output re-quantised 1x128, untimed glue). ue: power-of-two scales
+    through the *_ue8m0 calls. Returns a list of dicts (name, group, fn, flops, bytes,
+    padded_flops, extra)."""
     import torch
     import moe_grouped_gemm_fp32_amd as fg
     import synth
 
-    dev = torch.device("cuda:0")
     cases = []
-    ue = bool(args.ue8m0)
     kind = "pow2" if ue else "normal"
 
-    def add(name, fn, m_live, g_active, N, K, m_padded=None, extra=None):
+    def add(name, group, fn, m_live, g_active, N, K, m_padded=None, extra=None):
         flops, nbytes, padded = grouped_work(m_live, g_active, N, K, m_padded)
-        cases.append(dict(name=name, fn=fn, flops=flops, bytes=nbytes, padded_flops=padded, extra=extra or {}))
+        cases.append(dict(name=name, group=group, fn=fn, flops=flops, bytes=nbytes, padded_flops=padded,
+                          extra=extra or {}))
 
-    # C3: contiguous, groups of equal size (multiples of 128 rows: no padding rows)
+    # contiguous, groups of equal size (multiples of 128 rows: no padding rows)
     for G, rows, N, K in ((4, 8192, 4096, 7168), (8, 4096, 7168, 2048)):
         c = synth.contiguous_case([rows] * G, N, K, seed=3000 + G, device=dev, kind=kind)
         ws = fg.make_workspace(fg.KIND_CONTIGUOUS, c["M"], N, K, G, device=dev)
         cfg = fg.query_config(fg.KIND_CONTIGUOUS, c["M"], N, K, G)
-        add("contiguous G=%d x %d rows N=%d K=%d" % (G, rows, N, K),
+        add("contiguous G=%d x %d rows N=%d K=%d" % (G, rows, N, K), "contiguous",
             (lambda c=c, ws=ws: fg.fp8_grouped_gemm_nt_contiguous(c["A"], c["sa"], c["B"], c["sb"], c["D"],
                                                                   c["m_indices"], ws, ue8m0=ue)),
             G * rows, G, N, K, extra={"tile": "%dx%d" % (cfg["block_m"], cfg["block_n"]), "split_k": cfg["split_k"]})
-    # C4: masked decode, masked_m[g] uniform in [179, 333], M_max 4096, expected_m 256
+    # masked decode
     for N, K in ((4096, 7168), (7168, 2048)):
         for G in (1, 2, 4, 8, 16):
             c = synth.masked_case(G, 4096, N, K, seed=4000 + G + N, device=dev, expected_m=256, kind=kind)
             mm = c["masked_m_list"]
             cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
-            add("masked G=%d N=%d K=%d" % (G, N, K),
+            add("masked G=%d N=%d K=%d" % (G, N, K), "masked decode",
                 (lambda c=c: fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"], c["D"],
                                                            c["masked_m"], 256, ue8m0=ue)),
                 sum(mm), sum(1 for v in mm if v > 0), N, K,
                 extra={"masked_m_sum": sum(mm), "tile": "%dx%d" % (cfg["block_m"], cfg["block_n"])})
-    # C5: MoE FFN pair over 256 experts, 4096 tokens, top-8 Zipf(1.1) routing; the
-    # down GEMM's input is the SwiGLU of the gate+up output re-quantised 1x128 (untimed glue)
+    # MoE FFN pair
     c1 = synth.moe_case(seed=5000, device=dev, N=4096, K=7168, kind=kind)
     mi = c1["m_indices"]
     m_live = int((mi >= 0).sum())
@@ -336,61 +387,47 @@ def grouped_bench(args):
     D2 = synth.sentinel_output((c1["M"], 7168), dev)
     ws2 = fg.make_workspace(fg.KIND_CONTIGUOUS, c1["M"], 7168, 2048, 256, device=dev)
     fn2 = lambda: fg.fp8_grouped_gemm_nt_contiguous(A2, sa2, B2, sb2, D2, mi, ws2, ue8m0=ue)
-    add("moe gate+up (256 experts, %d live / %d padded rows) N=4096 K=7168" % (m_live, c1["M"]), fn1,
-        m_live, g_act, 4096, 7168, m_padded=c1["M"])
-    add("moe down (256 experts, %d live / %d padded rows) N=7168 K=2048" % (m_live, c1["M"]), fn2,
-        m_live, g_act, 7168, 2048, m_padded=c1["M"])
+    add("moe gate+up (256 experts, %d live / %d padded rows) N=4096 K=7168" % (m_live, c1["M"]), "MoE FFN pair",
+        fn1, m_live, g_act, 4096, 7168, m_padded=c1["M"])
+    add("moe down (256 experts, %d live / %d padded rows) N=7168 K=2048" % (m_live, c1["M"]), "MoE FFN pair",
+        fn2, m_live, g_act, 7168, 2048, m_padded=c1["M"])
     torch.cuda.synchronize()
+    return cases
 
-    def step(events=None):
-        for i, c in enumerate(cases):
-            if events is not None:
-                events[i][0].record()
-            c["fn"]()
-            if events is not None:
-                events[i][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
-    per = [0.0] * len(cases)
-    step()
-    all_ev = []
-    for _ in range(args.steps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
-        step(ev)
-        all_ev.append(ev)
-    torch.cuda.synchronize()
-    for ev in all_ev:
-        for i, (a, b) in enumerate(ev):
-            per[i] += a.elapsed_time(b)
-    rows, total = [], 0.0
-    for i, c in enumerate(cases):
-        ms = per[i] / args.steps
-        total += c["flops"]
+def grouped_rows(cases, per_ms):
+    rows = []
+    for c, ms in zip(cases, per_ms):
         bound, t_ideal = classify(c["flops"], c["bytes"])
         tflops = c["flops"] / (ms * 1e-3) / 1e12
         gbs = c["bytes"] / (ms * 1e-3) / 1e9
         frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
-        r = {"case": c["name"], "us": round(ms * 1e3, 2), "tflops": round(tflops, 1), "gbs": round(gbs, 1),
-             "bound": bound, "frac": round(frac, 4), "ideal_us": round(t_ideal * 1e6, 2),
+        r = {"config": c["group"], "case": c["name"], "us": round(ms * 1e3, 2), "tflops": round(tflops, 1),
+             "gbs": round(gbs, 1), "bound": bound, "frac": round(frac, 4), "ideal_us": round(t_ideal * 1e6, 2),
              "padded_tflops": round(c["padded_flops"] / (ms * 1e-3) / 1e12, 1),
              "algo_bytes": c["bytes"], "algo_flops": c["flops"]}
         r.update(c["extra"])
         rows.append(r)
+    return rows
+
+
+def grouped_bench(args):
+    """--workload grouped: the M-grouped workloads alone (one step = every case once).
+    Prints one JSON line (not the default benchmark, which includes these cases too)."""
+    import torch
+    dev = torch.device("cuda:0")
+    ue = bool(args.ue8m0)
+    cases = grouped_cases(dev, ue)
+    ms_per_step, per = time_cases([c["fn"] for c in cases], args.steps, args.warmup)
+    total = sum(c["flops"] for c in cases)
     out = {"metric": METRIC, "value": round(total / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
            "data": "synthetic",
-           "config": {"workload": ("UE8M0-scaled " if ue else "") + "M-grouped FP8 NT GEMMs: contiguous (4x8192 rows N=4096 K=7168; 8x4096 rows "
-                                  "N=7168 K=2048), masked decode (G in 1..16, M_max 4096, masked_m in [179,333]), "
-                                  "MoE FFN pair (4096 tokens, 256 experts, top-8 Zipf 1.1)"},
-           "per_case": rows}
+           "config": {"workload": ("UE8M0-scaled " if ue else "") + "M-grouped FP8 NT GEMMs: contiguous (4x8192 rows "
+                                  "N=4096 K=7168; 8x4096 rows N=7168 K=2048), masked decode (G in 1..16, M_max 4096, "
+                                  "masked_m in [179,333]), MoE FFN pair (4096 tokens, 256 experts, top-8 Zipf 1.1)"},
+           "per_case": grouped_rows(cases, per)}
     print(json.dumps(out), flush=True)
 
 
@@ -601,6 +638,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="default run without the small dense case and the grouped (contiguous, masked, MoE) rows")
     ap.add_argument("--with-c", action="store_true",
                     help="dense workload as D = C + A B^T with a BF16 C per shape (fp8_gemm_nt_c)")
     ap.add_argument("--ue8m0", action="store_true",
@@ -686,46 +725,16 @@ def main():
         cases.append(c)
     torch.cuda.synchronize()
 
-    def step(events=None):
-        for i, c in enumerate(cases):
-            if events is not None:
-                events[i][0].record()
-            if tn:
-                getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"], ue8m0=ue8m0)
-            elif c["C"] is not None:
-                fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
-            else:
-                gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
-            if events is not None:
-                events[i][1].record()
+    def call(c):
+        if tn:
+            getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"], ue8m0=ue8m0)
+        elif c["C"] is not None:
+            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
+        else:
+            gemm(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region 1: whole steps (value / ms_per_step)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-
-    # timed region 2: per-kernel durations with events on the launch stream. One
-    # untimed step goes first and nothing synchronises until the end, so the host
-    # stays ahead of the GPU and no event pair includes host launch latency.
-    per = [[0.0] for _ in cases]
-    step()
-    all_ev = []
-    for _ in range(args.steps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cases]
-        step(ev)
-        all_ev.append(ev)
-    torch.cuda.synchronize()
-    for ev in all_ev:
-        for i, (a, b) in enumerate(ev):
-            per[i][0] += a.elapsed_time(b)
+    ms_per_step, per_ms = time_cases([(lambda c=c: call(c)) for c in cases], args.steps, args.warmup)
+    per = [[ms * args.steps] for ms in per_ms]
     traffic = {}
     if os.path.exists(args.traffic_file):
         with open(args.traffic_file) as f:
@@ -767,8 +776,51 @@ def main():
     roof["avg_us"] = dom["us"]
     roof["algo_per_launch"] = dom["algo_flops"] if dom["bound"] == "mfma" else dom["algo_bytes"]
 
+    roof["avg_us_source"] = ("mean of HIP event pairs around each launch, recorded on the launch stream over "
+                             "the timed steps")
+
+    extra_rows = []
+    default_run = not ue8m0 and not args.with_c and not tn and not args.shapes
+    if default_run:
+        for r in rows:
+            r["config"] = "dense DeepSeek-V3 shape list"
+        # the small dense case: launch-latency-bound (its ideal time is ~0.03 us), so its
+        # row reports the per-call time and no roofline fraction
+        sm = synth.dense_case(128, 256, 512, seed=1001, device=dev)
+        f_s, b_s = algo_work(128, 256, 512)
+        # 200 back-to-back calls through the C ABI with pre-bound arguments between two
+        # events: the host issues a call in a few microseconds, so the GPU sets the pace
+        import ctypes
+        vp = ctypes.c_void_p
+        cargs = (vp(sm["A"].data_ptr()), sm["A"].stride(0), vp(sm["sa"].data_ptr()), sm["sa"].stride(0),
+                 vp(sm["B"].data_ptr()), sm["B"].stride(0), vp(sm["sb"].data_ptr()), vp(sm["D"].data_ptr()),
+                 sm["D"].stride(0), 128, 256, 512, None, 0, vp(torch.cuda.current_stream().cuda_stream))
+        raw = fg.lib().fp8_gemm_nt
+        assert raw(*cargs) == 0
+        n_small, reps = 200, []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(n_small):
+                raw(*cargs)
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / n_small)
+        sm_ms = sorted(reps)[len(reps) // 2]
+        extra_rows.append({"config": "dense small", "M": 128, "N": 256, "K": 512, "us": round(sm_ms * 1e3, 2),
+                           "tflops": round(f_s / sm_ms / 1e9, 2), "gbs": round(b_s / sm_ms / 1e6, 1),
+                           "bound": "latency", "frac": None,
+                           "note": "launch-latency-bound (ideal %.3f us): per-call time of 200 back-to-back calls, "
+                                   "no roofline fraction" % (b_s / 8e12 * 1e6),
+                           "algo_bytes": b_s, "algo_flops": f_s})
+        if not args.no_grouped:
+            gcases = grouped_cases(dev)
+            _, gper = time_cases([c["fn"] for c in gcases], args.steps, args.warmup)
+            extra_rows += grouped_rows(gcases, gper)
+
     cpu = None
-    if not args.no_cpu_baseline and not ue8m0 and not args.with_c and not tn:
+    if not args.no_cpu_baseline and default_run:
         cpu = cpu_baseline()
 
     out = {
@@ -784,7 +836,7 @@ def main():
                    "shapes": ["%dx%dx%d" % s for s in shapes]},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "per_shape": rows,
+        "per_shape": rows + extra_rows,
     }
     print(json.dumps(out), flush=True)
 

@@ -258,8 +258,14 @@ int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, 
  *   masked_m int32 [G] on the device: rows [0, masked_m[g]) of group g are
  *      computed; rows at or beyond it are not written. Values are clamped to
  *      [0, M_max]. The host never reads masked_m, so the call is graph-capturable.
- *   expected_m: host-side hint of the typical masked_m (tile choice only).
+ *   expected_m: host-side hint of the typical masked_m (tile choice and split-K
+ *      workspace size).
  *   G <= 1024.
+ * Split-K workspace: optional, as for the other calls. Its partials are sized for the
+ * live tiles of up to twice expected_m rows per group (fp8_gemm_workspace_size with
+ * FP8GEMM_KIND_MASKED and the same expected_m); a call whose masked_m hold more live
+ * tiles than the workspace fits runs without split-K (decided on the device; the
+ * results do not depend on it beyond FP32 summation order).
  */
 int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                                const void* B, int64_t ldb, const float* sb,

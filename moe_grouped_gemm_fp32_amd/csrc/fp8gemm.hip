@@ -85,6 +85,7 @@ constexpr size_t kScratchPartialBytes = (size_t)32 << 20;  // covers every plan 
 
 struct Plan {
   int bm = 128, bn = 128, split = 1, kbps = 1, tiles_m = 0, tiles_n = 0;
+  int64_t ws_tiles = 0;  // split tiles the workspace is sized for
   int64_t full = 0;  // leading tiles computed whole (the others are split `split` ways)
   int64_t units = 0;
   int grid = 0;
@@ -186,6 +187,14 @@ UnitCost unit_cost(int bm, int bn) {
   return {8.5, 0.88};  // 128x256
 }
 
+// Masked calls learn their live rows on the device; their split-K workspace is sized for
+// up to twice expected_m rows per group (masked_m spread around expected_m), and a call
+// with more live tiles than that runs unsplit (the kernel decides).
+int64_t masked_capacity_tiles(int G, int M_max, int N, int expected_m, int bm, int bn) {
+  const int64_t rows = std::min<int64_t>(M_max, 2 * (int64_t)std::max(expected_m > 0 ? expected_m : M_max, 1));
+  return (int64_t)G * ceil_div(rows, bm) * ceil_div(N, bn);
+}
+
 // Choose tile shape and split for a call. `rows` is M (dense), M_total
 // (contiguous) or M_max (masked, where expected_m estimates the live rows).
 Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
@@ -198,13 +207,15 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
     pl.full = std::max(0, g_forced_cfg.full_tiles);
   } else {
     double best = 1e30, best_units = 1e30;
-    const int live = kind == FP8GEMM_KIND_MASKED ? std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows))
-                                                 : rows;
+    const bool masked = kind == FP8GEMM_KIND_MASKED;
+    const int live = masked ? std::max(1, std::min(expected_m > 0 ? expected_m : rows, rows)) : rows;
     // candidate: `full` tiles computed whole, the other tiles split `split` ways
     auto consider = [&](const Variant& v, int64_t tiles, int split, int64_t full) {
       const int kbps = (int)ceil_div(num_kb, split);
       const int64_t split_tiles = split > 1 ? tiles - full : 0;
-      if (split > 1 && (split_tiles > kMaxSplitTiles || split_ws_bytes(split_tiles, split, v.bm, v.bn) > ws_avail))
+      // masked: the workspace must hold the live tiles of up to twice expected_m rows per group
+      const int64_t ws_tiles = masked ? masked_capacity_tiles(G, rows, N, expected_m, v.bm, v.bn) : split_tiles;
+      if (split > 1 && (ws_tiles > kMaxSplitTiles || split_ws_bytes(ws_tiles, split, v.bm, v.bn) > ws_avail))
         return;
       const UnitCost c = unit_cost(v.bm, v.bn);
       const double reduce =
@@ -216,8 +227,9 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
         const int64_t units = split > 1 ? tiles * split : tiles;
         t_units = (double)ceil_div(units, cus) * (c.fixed_us + (split > 1 ? kbps : num_kb) * c.kb_us + reduce);
       }
-      const double hbm_bytes = (double)rows * K * (kind == FP8GEMM_KIND_MASKED ? G : 1) +
-                               (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) + 2.0 * rows * N +
+      const double rows_live = masked ? (double)live * G : (double)rows;
+      const double hbm_bytes = rows_live * K + (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) +
+                               2.0 * rows_live * N +
                                8.0 * split * split_tiles * v.bm * v.bn;
       const double t = std::max(t_units, hbm_bytes / kHbmBytesPerUs);
       // ties of the bound (calls that stream the same bytes) go to the faster units
@@ -239,13 +251,13 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
           kind == FP8GEMM_KIND_MASKED && G > 1
               ? (int64_t)std::ceil((double)G * ceil_div(N, v.bn) * ((double)live / v.bm + kMaskedTileSlack))
               : ceil_div(live, v.bm) * ceil_div(N, v.bn) * (kind == FP8GEMM_KIND_MASKED ? G : 1);
-      const int max_split = kind == FP8GEMM_KIND_MASKED ? 1 : std::min(num_kb, kMaxSplit);
+      const int max_split = std::min(num_kb, kMaxSplit);
       const int64_t rem = tiles % cus;  // tiles of a last, partial round
       for (int sp = 1; sp <= max_split; ++sp) {
         if ((int)ceil_div(num_kb, ceil_div(num_kb, sp)) != sp) continue;  // same as a smaller split
         consider(v, tiles, sp, 0);
         // whole tiles for the full rounds, the last partial round split over the CUs
-        if (sp > 1 && tiles > cus && rem > 0 && rem * sp <= cus) consider(v, tiles, sp, tiles - rem);
+        if (!masked && sp > 1 && tiles > cus && rem > 0 && rem * sp <= cus) consider(v, tiles, sp, tiles - rem);
       }
     }
   }
@@ -254,9 +266,12 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   pl.tiles_n = (int)ceil_div(N, pl.bn);
   pl.tiles_m = (int)ceil_div(rows, pl.bm);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (kind == FP8GEMM_KIND_MASKED ? G : 1);
-  pl.full = pl.split > 1 && kind != FP8GEMM_KIND_MASKED ? std::min<int64_t>(pl.full, tiles) : tiles;
-  pl.ws_bytes = split_ws_bytes(tiles - pl.full, pl.split, pl.bm, pl.bn);
-  if (pl.split > 1 && (pl.ws_bytes > ws_avail || tiles - pl.full > kMaxSplitTiles) && !g_forced) {
+  // masked: every tile is split (no whole-tile rounds); the tile count is an upper bound
+  pl.full = pl.split > 1 ? (kind == FP8GEMM_KIND_MASKED ? 0 : std::min<int64_t>(pl.full, tiles)) : tiles;
+  pl.ws_tiles = kind == FP8GEMM_KIND_MASKED ? masked_capacity_tiles(G, rows, N, expected_m, pl.bm, pl.bn)
+                                            : tiles - pl.full;
+  pl.ws_bytes = split_ws_bytes(pl.ws_tiles, pl.split, pl.bm, pl.bn);
+  if (pl.split > 1 && (pl.ws_bytes > ws_avail || pl.ws_tiles > kMaxSplitTiles) && !g_forced) {
     pl.split = 1;
     pl.kbps = num_kb;
     pl.full = tiles;
@@ -359,7 +374,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   const size_t ws_avail = workspace ? workspace_bytes : 0;
   Plan pl = choose(kind, rows, N, K, G, expected_m, cus, ws_avail);
   if (!has_kernel(pl.bm, pl.bn)) return FP8GEMM_ERR_CONFIG;
-  if (pl.split > 1 && pl.units - pl.full > kMaxSplitTiles * pl.split) return FP8GEMM_ERR_CONFIG;
+  if (pl.split > 1 && pl.ws_tiles > kMaxSplitTiles) return FP8GEMM_ERR_CONFIG;
   if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
   maybe_print(name, rows, N, K, G, pl);
   p.N = N;
@@ -380,6 +395,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   if (pl.split > 1) {
     p.counters = static_cast<int32_t*>(workspace);
     p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    p.ws_tiles = (int)pl.ws_tiles;
   }
   if (pl.units == 0) return FP8GEMM_OK;
   // one tile row covers all of M (dense): each B tile is read by one unit only
@@ -436,14 +452,13 @@ int grouped_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_s
 
 int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                    const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G, int M_max, int N, int K,
-                   int expected_m, hipStream_t stream, bool e8, const void* C = nullptr, int64_t ldc = 0,
-                   bool packed = false) {
+                   int expected_m, void* workspace, size_t workspace_bytes, hipStream_t stream, bool e8,
+                   const void* C = nullptr, int64_t ldc = 0, bool packed = false) {
   int st = check_common(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M_max, N, K);
   if (st == FP8GEMM_OK) st = check_c(C, ldc, N);
   if (st != FP8GEMM_OK) return st;
   if (!masked_m) return FP8GEMM_ERR_NULL;
   if (G <= 0 || G > fp8gemm::kMaxGroups || M_max <= 0) return FP8GEMM_ERR_SHAPE;
-  if (g_forced && g_forced_cfg.split_k > 1) return FP8GEMM_ERR_CONFIG;  // masked never splits K
   Params p = base_params(A, lda, sa, ld_sa, B, ldb, sb, D, ldd);
   p.M = M_max;
   p.masked_m = masked_m;
@@ -457,7 +472,7 @@ int grouped_masked(const void* A, int64_t lda, const float* sa, int64_t ld_sa, c
   p.ldc = ldc;
   p.c_gstride = (int64_t)M_max * ldc;
   return run(FP8GEMM_KIND_MASKED, e8 ? (packed ? "masked ue8m0 packed" : "masked ue8m0") : "masked", p, M_max, N,
-             K, G, expected_m, nullptr, 0, stream, e8);
+             K, G, expected_m, workspace, workspace_bytes, stream, e8);
 }
 
 }  // namespace
@@ -547,10 +562,9 @@ int fp8_grouped_gemm_nt_masked_ue8m0_packed(const void* A, int64_t lda, const in
                                             const void* B, int64_t ldb, const int32_t* sb, void* D, int64_t ldd,
                                             const int32_t* masked_m, int G, int M_max, int N, int K, int expected_m,
                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return grouped_masked(A, lda, reinterpret_cast<const float*>(sa), ld_sa, B, ldb, reinterpret_cast<const float*>(sb),
-                        D, ldd, masked_m, G, M_max, N, K, expected_m, stream, true, nullptr, 0, true);
+                        D, ldd, masked_m, G, M_max, N, K, expected_m, workspace, workspace_bytes, stream, true, nullptr,
+                        0, true);
 }
 
 int fp8_grouped_gemm_nt_contiguous(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
@@ -581,9 +595,8 @@ int fp8_grouped_gemm_nt_masked_c(const void* A, int64_t lda, const float* sa, in
                                  int64_t ldb, const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd,
                                  const int32_t* masked_m, int G, int M_max, int N, int K, int expected_m,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, false,
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, workspace,
+                        workspace_bytes, stream, false,
                         C, ldc);
 }
 
@@ -591,18 +604,16 @@ int fp8_grouped_gemm_nt_masked(const void* A, int64_t lda, const float* sa, int6
                                int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* masked_m, int G,
                                int M_max, int N, int K, int expected_m, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, false);
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, workspace,
+                        workspace_bytes, stream, false);
 }
 
 int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B,
                                      int64_t ldb, const float* sb, void* D, int64_t ldd, const int32_t* masked_m,
                                      int G, int M_max, int N, int K, int expected_m, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, stream, true);
+  return grouped_masked(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, masked_m, G, M_max, N, K, expected_m, workspace,
+                        workspace_bytes, stream, true);
 }
 
 int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t ldq, float* sa, int64_t ld_sa, int M,
@@ -878,7 +889,7 @@ int fp8_transform_sf_into_required_layout(const float* sf, int64_t ld_sf, int ro
 }
 
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 128 || kind == FP8GEMM_KIND_MASKED) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
   int st;
   const int cus = effective_cus(false, &st);
   const Plan pl = choose(kind, M, N, K, std::max(G, 1), expected_m, cus, SIZE_MAX);
@@ -891,8 +902,7 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m, 
   if (M < 0 || N <= 0 || K <= 0 || K % 128 || G <= 0) return FP8GEMM_ERR_SHAPE;
   int st;
   const int cus = effective_cus(false, &st);
-  const Plan pl = choose(kind, M, N, K, G, expected_m, cus,
-                         kind == FP8GEMM_KIND_MASKED ? 0 : workspace_bytes);
+  const Plan pl = choose(kind, M, N, K, G, expected_m, cus, workspace_bytes);
   out->block_m = pl.bm;
   out->block_n = pl.bn;
   out->split_k = pl.split;

@@ -69,6 +69,8 @@ struct Params {
   int sb_kstride;            // entries per weight-scale row: K/128 (FP32) or ceil(K/512) (packed)
   float* ws;                 // split-K partials [split tile][split][BM*BN]
   int32_t* counters;         // split-K arrival counters [split tile]
+  int ws_tiles;              // split tiles the workspace holds (masked: a call whose live tiles exceed
+                             // it runs unsplit)
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -364,7 +366,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   const int wave = uni(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  const int S = p.split_k;
+  int S = p.split_k;
 
   // ---- masked: live m-tiles per group, exclusive prefix sum in LDS
   int num_units = p.num_units;
@@ -398,7 +400,11 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     }
     if (tid == NT - 1) s_pre[min(p.G, kMaxGroups)] = s_scan[NT - 1];
     __syncthreads();
-    num_units = s_pre[p.G] * p.tiles_n * S;
+    // the live tiles are known only here: split K only if the workspace holds them all
+    // (the same decision in every workgroup)
+    const int live_total = uni(s_pre[p.G]) * p.tiles_n;
+    if (S > 1 && live_total > p.ws_tiles) S = 1;
+    num_units = live_total * S;
   }
 
   for (int u = blockIdx.x; u < num_units; u += gridDim.x) {
@@ -428,6 +434,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       const int r = local - tn * live_tiles * S;
       tm = r / S;
       split = r - tm * S;
+      ws_id = pre * p.tiles_n + tn * live_tiles + tm;  // this live tile's slot, < live_total
     } else {
       // the first full_tiles tiles are single units; each later one is S units, so a
       // last partial round of tiles can be spread over all CUs as K slices. Split

@@ -132,8 +132,16 @@ def test_planner_masked_and_contiguous(cus256):
     for G in (1, 2, 4, 8, 16):
         for N, K in ((4096, 7168), (7168, 2048)):
             cfg = fg.query_config(fg.KIND_MASKED, 4096, N, K, G, expected_m=256)
-            assert cfg["split_k"] == 1 and cfg["block_m"] in (64, 128, 256)
-            assert fg.workspace_size(fg.KIND_MASKED, 4096, N, K, G, 256) == 0
+            assert cfg["block_m"] in (64, 128, 256)
+            ws = fg.workspace_size(fg.KIND_MASKED, 4096, N, K, G, 256)
+            assert (ws > 0) == (cfg["split_k"] > 1)
+            # the workspace holds the live tiles of twice expected_m rows per group
+            if cfg["split_k"] > 1:
+                cap = G * -(-512 // cfg["block_m"]) * -(-N // cfg["block_n"])
+                assert ws == 16384 + cap * cfg["split_k"] * cfg["block_m"] * cfg["block_n"] * 4
+                assert cfg["full_tiles"] == 0
+            # without a workspace the masked call does not split
+            assert fg.query_config(fg.KIND_MASKED, 4096, N, K, G, 256, workspace_bytes=0)["split_k"] == 1
     cfg = fg.query_config(fg.KIND_CONTIGUOUS, 32768, 4096, 7168, 4)
     assert 128 % cfg["block_m"] == 0
 

@@ -222,3 +222,51 @@ def test_masked_rejects_too_many_groups():
     st = fg.lib().fp8_grouped_gemm_nt_masked(P(1 << 20), 256, P(1 << 20), 32, P(1 << 20), 256, P(1 << 20),
                                              P(1 << 20), 256, P(1 << 20), 1025, 32, 256, 256, 16, None, 0, None)
     assert st == -2
+
+
+@pytest.mark.parametrize("tile", [(64, 64, 2), (128, 128, 4), (256, 128, 3), (128, 256, 2), (64, 128, 8), (128, 64, 5)],
+                         ids=lambda t: "%dx%d_s%d" % t)
+@pytest.mark.parametrize("kind", ["normal", "e1", "e1-ue8m0"])
+def test_masked_split_k_forced(cuda_device, tile, kind):
+    """Masked calls split K too (a K slice per unit, partials reduced by the last arrival
+    into the live tile's workspace slot): empty, partial and full groups."""
+    mm = [0, 300, 512, 1]
+    ue = kind.endswith("ue8m0")
+    kind = kind.split("-")[0]
+    c = synth.masked_case(4, 512, 384, 1152, seed=9100 + tile[0] + tile[2], device=cuda_device, masked_m=mm,
+                          expected_m=256, kind=kind)
+    nbytes = forced_workspace_bytes(fg.KIND_MASKED, 512, 384, 1152, 4, tile)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=cuda_device)
+    ref, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm, d_bits(c))
+    for call in range(2):   # the workspace is reused
+        D = c["D"].clone()
+        with fg.force_config(*tile):
+            fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"], D, c["masked_m"], 256, ws, ue8m0=ue)
+        torch.cuda.synchronize()
+        got = bits_of(D)
+        for g, live in enumerate(mm):
+            assert np.all(got[g, live:] == SENT), f"dead rows of group {g} written"
+            compare(kind, got[g, :live], ref[g, :live], f"masked split {tile} ue8m0={ue} group {g} call {call}")
+        assert int(ws[:16384].count_nonzero()) == 0, "split-K counters must be left at zero"
+
+
+def test_masked_split_k_falls_back_when_live_tiles_exceed_the_workspace(cuda_device):
+    """The workspace is sized for twice expected_m rows per group; a call whose groups hold
+    more live tiles than that runs unsplit on the device, with the same results."""
+    mm = [500, 512, 450]
+    c = synth.masked_case(3, 512, 256, 1024, seed=9200, device=cuda_device, masked_m=mm, expected_m=32)
+    tile = (64, 64, 4)
+    with fg.force_config(*tile):
+        small = fg.workspace_size(fg.KIND_MASKED, 512, 256, 1024, 3, 32)   # capacity: 64 rows per group
+    assert small > 16384
+    ws = torch.zeros(small, dtype=torch.uint8, device=cuda_device)
+    D = c["D"].clone()
+    with fg.force_config(*tile):
+        fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"], D, c["masked_m"], 32, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.grouped_masked(*host(c, "A", "sa", "B", "sb"), mm, d_bits(c))
+    got = bits_of(D)
+    for g, live in enumerate(mm):
+        assert np.all(got[g, live:] == SENT)
+        compare("normal", got[g, :live], ref[g, :live], f"fallback group {g}")
+    assert int(ws[:16384].count_nonzero()) == 0
