@@ -411,6 +411,115 @@ def grouped_rows(cases, per_ms):
     return rows
 
 
+def plan_sweep(args):
+    """--plan-sweep dense|masked: time every tile / split (/ whole-tile-round) plan of each
+    dense shape or masked decode case, forced for that call only, inside the benchmark's
+    sequence of calls (the other calls keep their own plans). Rounds are enqueued without
+    synchronising, so the GPU stays busy as in the benchmark; the median event time over
+    `--rounds` rounds (after one untimed round) is printed per plan, one JSON line per case.
+    The planner's cost constants are fitted to these tables (--plan-table)."""
+    import numpy as np
+    import torch
+    import moe_grouped_gemm_fp32_amd as fg
+    import synth
+    dev = torch.device("cuda:0")
+    WS = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)   # one workspace, shared by every call in turn
+    if args.plan_sweep == "dense":
+        cases = []
+        for i, (M, N, K) in enumerate(CONFIG2):
+            c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02)
+            cases.append(dict(key=[M, N, K], M=M, N=N, K=K, G=1, kind=fg.KIND_DENSE,
+                              fn=(lambda c=c: fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], WS))))
+    else:
+        cases = []
+        for N, K in ((4096, 7168), (7168, 2048)):
+            for G in (1, 2, 4, 8, 16):
+                c = synth.masked_case(G, 4096, N, K, seed=4000 + G + N, device=dev, expected_m=256)
+                cases.append(dict(key=[G, N, K], M=4096, N=N, K=K, G=G, kind=fg.KIND_MASKED,
+                                  fn=(lambda c=c: fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"],
+                                                                                c["D"], c["masked_m"], 256, WS))))
+    torch.cuda.synchronize()
+    tiles = [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128), (128, 256)]
+    for ti, t in enumerate(cases):
+        nkb = t["K"] // 128
+        masked = t["kind"] == fg.KIND_MASKED
+        cands = [None]
+        for bm, bn in tiles:
+            if not masked and ((t["M"] <= 128 and bm > 128) or (t["M"] > 128 and bm < 128)):
+                continue
+            ntiles = -(-t["M"] // bm) * -(-t["N"] // bn)
+            rem = ntiles % 256
+            for sp in ((1, 2, 3, 4, 6, 8) if masked else range(1, 9)):
+                if -(-nkb // -(-nkb // sp)) != sp:
+                    continue
+                if masked or ntiles * sp <= 1024 or sp == 1:
+                    cands.append((bm, bn, sp, 0))
+                if not masked and sp > 1 and ntiles > 256 and rem > 0 and rem * sp <= 256:
+                    cands.append((bm, bn, sp, ntiles - rem))
+        res = {}
+        for cfg in cands:
+            if cfg is not None:
+                try:
+                    with fg.force_config(*cfg[:3], full_tiles=cfg[3]):
+                        t["fn"]()
+                except Exception:
+                    continue   # a plan the library rejects (too many split tiles)
+            evs = []
+            for r in range(args.rounds + 1):
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for ci, c in enumerate(cases):
+                    if ci == ti:
+                        ev[0].record()
+                        if cfg is None:
+                            c["fn"]()
+                        else:
+                            with fg.force_config(*cfg[:3], full_tiles=cfg[3]):
+                                c["fn"]()
+                        ev[1].record()
+                    else:
+                        c["fn"]()
+                evs.append(ev)
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in evs[1:]]))
+            key = "auto" if cfg is None else ("%dx%d s%d" % cfg[:3] if masked else "%dx%d s%d f%d" % cfg)
+            res[key] = round(ms * 1e3, 2)
+        print(json.dumps({"kind": args.plan_sweep, "case": t["key"], "all": res}), flush=True)
+
+
+def plan_table(args):
+    """--plan-table LOG...: average (geometric mean) the --plan-sweep logs of several runs
+    into profiles/planner_sweep.json, the measured table the planner is checked against."""
+    import math
+    import platform
+    acc = {"dense": {}, "masked": {}}
+    runs = {"dense": 0, "masked": 0}
+    for f in args.plan_table:
+        with open(f) as fh:
+            kinds = set()
+            for line in fh:
+                if not line.startswith("{"):
+                    continue
+                d = json.loads(line)
+                kinds.add(d["kind"])
+                tab = acc[d["kind"]].setdefault(",".join(str(x) for x in d["case"]), {})
+                for k, v in d["all"].items():
+                    if k != "auto":
+                        tab.setdefault(k, []).append(v)
+            for k in kinds:
+                runs[k] += 1
+    out = {"what": "event time (us) of every plan of each case, forced for that call only inside the benchmark's "
+                   "sequence of calls; geometric mean over the runs",
+           "command": "python bench.py --plan-sweep dense --rounds 12 > LOG (twice, likewise --plan-sweep masked); "
+                      "python bench.py --plan-table LOG...",
+           "kernel_sha": kernel_source_hash(), "runs": runs}
+    for kind in ("dense", "masked"):
+        out[kind] = {case: {k: round(math.exp(sum(math.log(x) for x in v) / len(v)), 2) for k, v in tab.items()}
+                     for case, tab in acc[kind].items()}
+    with open(os.path.join(ROOT, "profiles", "planner_sweep.json"), "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(json.dumps({k: out[k] for k in ("what", "runs", "kernel_sha")}))
+
+
 def grouped_bench(args):
     """--workload grouped: the M-grouped workloads alone (one step = every case once).
     Prints one JSON line (not the default benchmark, which includes these cases too)."""
@@ -637,6 +746,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
+    ap.add_argument("--plan-sweep", choices=("dense", "masked"),
+                    help="time every plan of each dense shape / masked decode case (planner fitting)")
+    ap.add_argument("--rounds", type=int, default=12, help="rounds per plan of --plan-sweep")
+    ap.add_argument("--plan-table", nargs="+", metavar="LOG",
+                    help="average --plan-sweep logs into profiles/planner_sweep.json")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-grouped", action="store_true",
                     help="default run without the small dense case and the grouped (contiguous, masked, MoE) rows")
@@ -658,6 +772,12 @@ def main():
                     help="build the traffic table from rocprofv3 --pmc output directories")
     args = ap.parse_args()
 
+    if args.plan_table:
+        plan_table(args)
+        return
+    if args.plan_sweep:
+        plan_sweep(args)
+        return
     if args.pmc_summary:
         pmc_summary(args, parse_shapes(args.shapes) if args.shapes else CONFIG2)
         return

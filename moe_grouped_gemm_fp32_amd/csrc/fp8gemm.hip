@@ -159,32 +159,34 @@ size_t split_ws_bytes(int64_t split_tiles, int split, int bm, int bn) {
 // rounds * (unit cost) with rounds = ceil(units / CUs), so the planner trades tile
 // efficiency against filling all CUs (the unaligned-block argument of the pages:
 // deepep.org/zh/deepgemm, 非对齐块大小).
+// The constants were fitted to measured timings of every tile / split / whole-tile-round
+// candidate of the 18 dense DeepSeek-V3-like shapes and the 10 masked decode cases, each
+// timed inside the benchmark's sequence of calls (two runs averaged; bench.py --plan-sweep,
+// the table in profiles/planner_sweep.json): with them the chosen plan is within 4.5% of
+// the fastest measured one in all 28 cases.
 constexpr double kSplitUnitUs = 3.0;
 constexpr double kSplitReadUsPerKB = 0.03;
 // A call also takes at least its HBM traffic (A, B and D once, plus the split-K
-// partials, written and read once each) over the read rate measured when the
-// Infinity Cache holds dirty lines of an earlier output, as it does between
-// back-to-back GEMMs: about 2 TB/s. For few-row shapes, which stream B once, this
-// bound decides between tiles and splits that the per-unit costs rank wrongly.
-constexpr double kHbmBytesPerUs = 2.05e6;
+// partials, written and read once each) over an effective read rate of 3.5 TB/s, the
+// rate the few-row shapes (which stream B once) reach between back-to-back GEMMs. For
+// them this bound decides between tiles and splits that the per-unit costs rank wrongly.
+constexpr double kHbmBytesPerUs = 3.5e6;
 constexpr int kMaxSplit = 8;
 // Extra live M tiles per group the planner assumes for masked calls with several
-// groups. Fitted to timings of every tile shape on the masked decode configurations
-// (G in 1..16, masked_m spread over [179, 333], expected_m 256): with it the chosen tile
-// is within 2% of the fastest in all ten; the exact mean of ceil(masked_m / BM) there
-// is half a tile above expected_m / BM, but the round-based estimate over-charges a
-// nearly empty last round.
+// groups: their live rows differ, so ceil(masked_m / BM) averages above expected_m / BM
+// (by half a tile for masked_m spread over [179, 333]); a quarter because the round-based
+// estimate over-charges a nearly empty last round.
 constexpr double kMaskedTileSlack = 0.25;
 struct UnitCost {
   double fixed_us, kb_us;
 };
 UnitCost unit_cost(int bm, int bn) {
-  if (bm == 64 && bn == 64) return {5.0, 0.45};
-  if (bm == 128 && bn == 128) return {9.0, 0.53};
+  if (bm == 64 && bn == 64) return {4.4, 0.37};
+  if (bm == 128 && bn == 128) return {8.7, 0.64};
   if (bm == 128 && bn == 64) return {5.0, 0.60};
-  if (bm == 64 && bn == 128) return {4.0, 0.60};
-  if (bm == 256 && bn == 128) return {8.0, 0.88};
-  return {8.5, 0.88};  // 128x256
+  if (bm == 64 && bn == 128) return {4.2, 0.59};
+  if (bm == 256 && bn == 128) return {7.8, 0.85};
+  return {8.3, 0.88};  // 128x256
 }
 
 // Masked calls learn their live rows on the device; their split-K workspace is sized for
