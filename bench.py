@@ -37,11 +37,12 @@ CONFIG2 = [(m, n, k) for m in (64, 128, 4096)
            for (n, k) in ((2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048))]
 
 
-def algo_work(M, N, K, G=1):
-    """Algorithmic FLOPs and HBM bytes of one dense call (each operand read once, D written once)."""
+def algo_work(M, N, K, G=1, scale_bytes=4.0):
+    """Algorithmic FLOPs and HBM bytes of one dense call (each operand read once, D written
+    once); scale_bytes per block scale: 4 (FP32) or 1 (packed UE8M0, four codes a word)."""
     flops = 2.0 * M * N * K
     kb = K // 128
-    nbytes = M * K + G * N * K + M * N * 2 + M * kb * 4 + G * ((N + 127) // 128) * kb * 4
+    nbytes = int(M * K + G * N * K + M * N * 2 + (M * kb + G * ((N + 127) // 128) * kb) * scale_bytes)
     return flops, nbytes
 
 
@@ -74,6 +75,31 @@ def read_counter_csv(d, counter):
     return [(k, v) for _, k, v in rows]
 
 
+N_SMALL, SMALL_REPS = 200, 5   # the small dense case: SMALL_REPS groups of N_SMALL back-to-back calls
+
+
+def dispatch_blocks(n, shapes, steps, warmup):
+    """GEMM-kernel dispatch indices (in dispatch order) of one case each, for a profiled
+    default run of `steps` / `warmup`: the dense shapes step by step, then the small dense
+    case (one checking call, then its timed calls), then the untimed gate+up call that
+    makes the MoE down GEMM's input and the grouped cases step by step. A run with
+    --no-grouped holds the dense block only. The last `steps` dispatches of a case are the
+    ones its HIP-event time covers. Returns (dense, small, grouped) index lists."""
+    per = warmup + 2 * steps + 1
+    nd = len(shapes) * per
+    dense = [list(range(i, nd, len(shapes))) for i in range(len(shapes))]
+    if n == nd:
+        return dense, [], []
+    ng = len(GROUPED_CASES)
+    g0 = nd + 1 + N_SMALL * SMALL_REPS + 1
+    if n != g0 + ng * per:
+        sys.exit("%d GEMM dispatches in the trace; a run of --steps %d --warmup %d makes %d (dense only) or %d"
+                 % (n, steps, warmup, nd, g0 + ng * per))
+    small = list(range(nd + 1, nd + 1 + N_SMALL * SMALL_REPS))
+    grouped = [list(range(g0 + i, g0 + ng * per, ng)) for i in range(ng)]
+    return dense, small, grouped
+
+
 def pmc_summary(args, shapes):
     """Build the HBM-traffic table from FETCH_SIZE / WRITE_SIZE runs of this benchmark and of
     the plain copy (--copy-mb). Counters are KiB per dispatch; each is scaled by the ratio
@@ -88,12 +114,13 @@ def pmc_summary(args, shapes):
 
     ff = copy_factor(cfetch_dir, "FETCH_SIZE")
     fw = copy_factor(cwrite_dir, "WRITE_SIZE")
-    fetch = [v for k, v in read_counter_csv(fetch_dir, "FETCH_SIZE") if "fp8_gemm" in k]
-    write = [v for k, v in read_counter_csv(write_dir, "WRITE_SIZE") if "fp8_gemm" in k]
+    fetch = [v for k, v in read_counter_csv(fetch_dir, "FETCH_SIZE") if "fp8_gemm_kernel" in k]
+    write = [v for k, v in read_counter_csv(write_dir, "WRITE_SIZE") if "fp8_gemm_kernel" in k]
+    dense, _, _ = dispatch_blocks(len(fetch), shapes, args.steps, args.warmup)
     table = {}
     for i, (M, N, K) in enumerate(shapes):
-        f = fetch[i::len(shapes)]
-        w = write[i::len(shapes)]
+        f = [fetch[j] for j in dense[i]]
+        w = [write[j] for j in dense[i]]
         fk = sum(f) / len(f)
         wk = sum(w) / len(w)
         _, algo = algo_work(M, N, K)
@@ -135,9 +162,11 @@ def kg_pmc_summary(args):
     print(json.dumps(out))
 
 
-def trace_summary(d, shapes):
-    """Per-shape average GEMM kernel duration from a rocprofv3 --kernel-trace csv directory
-    (dispatch i of the GEMM kernel belongs to shape i mod len(shapes))."""
+def trace_summary(d, shapes, steps, warmup):
+    """Per-case GEMM kernel durations from a rocprofv3 --kernel-trace csv directory of a
+    default run with the same --steps / --warmup: the mean over all of a case's dispatches
+    and over the event-timed ones (the last `steps`), which the run's own HIP-event
+    figures cover."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     rows = []
     for f in files:
@@ -147,15 +176,29 @@ def trace_summary(d, shapes):
                     rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     rows.sort()
-    out = []
+    dense, small, grouped = dispatch_blocks(len(rows), shapes, steps, warmup)
+
+    def stats(idx):
+        sel = [rows[j] for j in idx]
+        timed = sel[-steps:]
+        return {"kernel": sel[0][1].replace("void fp8gemm::", ""), "dispatches": len(sel),
+                "avg_us": round(sum(r[2] for r in sel) / len(sel) / 1e3, 2),
+                "timed_avg_us": round(sum(r[2] for r in timed) / len(timed) / 1e3, 2)}
+
     for i, (M, N, K) in enumerate(shapes):
-        sel = rows[i::len(shapes)]
-        us = sum(r[2] for r in sel) / len(sel) / 1e3
+        o = {"M": M, "N": N, "K": K}
+        o.update(stats(dense[i]))
         flops, nbytes = algo_work(M, N, K)
-        out.append({"M": M, "N": N, "K": K, "kernel": sel[0][1].replace("void fp8gemm::", ""),
-                    "dispatches": len(sel), "avg_us": round(us, 2),
-                    "tflops": round(flops / us / 1e6, 1), "gbs": round(nbytes / us / 1e3, 1)})
-    for o in out:
+        o.update({"tflops": round(flops / o["timed_avg_us"] / 1e6, 1),
+                  "gbs": round(nbytes / o["timed_avg_us"] / 1e3, 1)})
+        print(json.dumps(o))
+    if small:
+        sel = [rows[j][2] for j in small]
+        print(json.dumps({"case": "dense small 128x256x512", "dispatches": len(sel),
+                          "avg_us": round(sum(sel) / len(sel) / 1e3, 2)}))
+    for name, idx in zip(GROUPED_CASES, grouped):
+        o = {"case": name}
+        o.update(stats(idx))
         print(json.dumps(o))
 
 
@@ -185,10 +228,10 @@ def trace_summary_grouped(d):
                           "dispatches": len(sel), "avg_us": round(us, 2)}))
 
 
-def counter_summary(d, shapes):
-    """Per-shape mean of every counter in a rocprofv3 --pmc csv directory of the dense
-    benchmark (GEMM dispatch i belongs to shape i mod len(shapes)); values are summed
-    over the counter's hardware instances within a dispatch."""
+def counter_summary(d, shapes, steps, warmup):
+    """Per-shape mean of every counter in a rocprofv3 --pmc csv directory of a default run
+    with the same --steps / --warmup (dense shapes only); values are summed over the
+    counter's hardware instances within a dispatch."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     per = {}
     for f in files:
@@ -200,8 +243,9 @@ def counter_summary(d, shapes):
                 per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     dispatches = sorted({k[0] for k in per})
     names = sorted({k[1] for k in per})
+    dense, _, _ = dispatch_blocks(len(dispatches), shapes, steps, warmup)
     for i, (M, N, K) in enumerate(shapes):
-        sel = dispatches[i::len(shapes)]
+        sel = [dispatches[j] for j in dense[i]]
         row = {"M": M, "N": N, "K": K, "dispatches": len(sel)}
         for c in names:
             vals = [per[(x, c)] for x in sel if (x, c) in per]
@@ -756,6 +800,9 @@ def main():
                     help="default run without the small dense case and the grouped (contiguous, masked, MoE) rows")
     ap.add_argument("--with-c", action="store_true",
                     help="dense workload as D = C + A B^T with a BF16 C per shape (fp8_gemm_nt_c)")
+    ap.add_argument("--packed", action="store_true",
+                    help="with --workload ue8m0: the scales packed four UE8M0 codes a word through "
+                         "fp8_gemm_nt_ue8m0_packed")
     ap.add_argument("--ue8m0", action="store_true",
                     help="with --workload grouped or kgrouped: power-of-two (UE8M0) scales through the *_ue8m0 calls")
     ap.add_argument("--accumulate", action="store_true", help="with --workload kgrouped: D += A^T B")
@@ -785,13 +832,15 @@ def main():
         kg_pmc_summary(args)
         return
     if args.counter_summary:
-        counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+        counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
+                        args.steps, args.warmup)
         return
     if args.trace_summary:
         if args.workload == "grouped":
             trace_summary_grouped(args.trace_summary)
         else:
-            trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2)
+            trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
+                          args.steps, args.warmup)
         return
     if args.copy_mb:
         copy_only(args)
@@ -822,11 +871,17 @@ def main():
     if tn and args.with_c:
         sys.exit("--layout %s takes no C" % args.layout)
     layout_fn = {"tn": "fp8_gemm_tn", "nn": "fp8_gemm_nn", "tt": "fp8_gemm_tt"}.get(args.layout)
-    gemm = fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
+    packed = ue8m0 and args.packed
+    if args.packed and not ue8m0:
+        sys.exit("--packed goes with --workload ue8m0")
+    gemm = fg.fp8_gemm_nt_ue8m0_packed if packed else fg.fp8_gemm_nt_ue8m0 if ue8m0 else fg.fp8_gemm_nt
     cases = []
     for i, (M, N, K) in enumerate(shapes):
         c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02,
                              kind="pow2" if ue8m0 else "normal")
+        if packed:  # sa [K/128, M] -> [ceil(K/512), M], sb [N/128, K/128] -> [N/128, ceil(K/512)]
+            c["sa"] = synth.pack_ue8m0(c["sa"], 0)
+            c["sb"] = synth.pack_ue8m0(c["sb"], 1)
         c["ws"] = fg.make_workspace(fg.KIND_DENSE, M, N, K, device=dev)
         c["C"] = (torch.randn(M, N, generator=synth.make_generator(2500 + i, dev), device=dev) * 0.1).to(
             torch.bfloat16) if args.with_c else None
@@ -865,7 +920,7 @@ def main():
     total_flops = 0.0
     rows = []
     for i, ((M, N, K), c) in enumerate(zip(shapes, cases)):
-        flops, nbytes = algo_work(M, N, K)
+        flops, nbytes = algo_work(M, N, K, scale_bytes=1.0 if packed else 4.0)
         if args.with_c:
             nbytes += 2 * M * N  # C read once
         total_flops += flops
@@ -917,8 +972,8 @@ def main():
                  sm["D"].stride(0), 128, 256, 512, None, 0, vp(torch.cuda.current_stream().cuda_stream))
         raw = fg.lib().fp8_gemm_nt
         assert raw(*cargs) == 0
-        n_small, reps = 200, []
-        for _ in range(5):
+        n_small, reps = N_SMALL, []
+        for _ in range(SMALL_REPS):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record()
@@ -950,7 +1005,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense FP8 %s GEMM with 1x128/128x128 %s scales and BF16 output over %d "
                                "DeepSeek-V3-like shapes (M in {64,128,4096} x (N,K) list)"
-                               % (args.layout.upper(), "UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
+                               % (args.layout.upper(), "packed UE8M0 (four codes a word)" if packed else
+                                  "UE8M0 (power-of-two)" if ue8m0 else "FP32", len(shapes))
                                + (", D = C + A B^T with a BF16 C" if args.with_c else "")
                                + (" (%s)" % layout_fn if tn else ""),
                    "shapes": ["%dx%dx%d" % s for s in shapes]},

@@ -54,9 +54,11 @@ def test_trace_summaries(tmp_path, capsys):
             d += 1
             rows.append([d, "void at::native::other_kernel()", 0, 99999])
     _write_csv(str(tmp_path / "t" / "run_kernel_trace.csv"), ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
-    bench.trace_summary(str(tmp_path / "t"), shapes)
+    bench.trace_summary(str(tmp_path / "t"), shapes, steps=1, warmup=0)
     out = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
     assert [o["avg_us"] for o in out] == [1.0, 2.0] and all(o["dispatches"] == 3 for o in out)
+    with pytest.raises(SystemExit):  # 6 dispatches cannot come from a run of --steps 2
+        bench.trace_summary(str(tmp_path / "t"), shapes, steps=2, warmup=0)
 
     # grouped: the first GEMM dispatch (the untimed gate+up call) is dropped
     n = len(bench.GROUPED_CASES)
@@ -70,19 +72,65 @@ def test_trace_summaries(tmp_path, capsys):
     assert len(out) == n and [o["avg_us"] for o in out] == [float(i + 1) for i in range(n)]
 
 
+def test_default_run_dispatch_layout(tmp_path, capsys):
+    """A default run's trace: dense shapes step by step, the small case (one checking call,
+    then its timed calls), the untimed gate+up call, the grouped cases step by step; the
+    event-timed mean covers each case's last `steps` dispatches."""
+    shapes = [(64, 256, 512), (128, 512, 1024)]
+    steps, warmup = 2, 1
+    per = warmup + 2 * steps + 1
+    n = len(bench.GROUPED_CASES)
+    gemm = "void fp8gemm::fp8_gemm_kernel<64, 64, 2, 2, 8, false>(fp8gemm::Params)"
+    rows, d = [], 0
+
+    def add(us):
+        nonlocal d
+        d += 1
+        rows.append([d, gemm, 0, int(us * 1000)])
+        d += 1
+        rows.append([d, "void at::native::other_kernel()", 0, 99999])
+
+    for rep in range(per):
+        for i in range(len(shapes)):
+            add(10 * (i + 1) + (5 if rep >= per - steps else 0))
+    add(1000)  # the small case's checking call
+    for _ in range(bench.N_SMALL * bench.SMALL_REPS):
+        add(3)
+    add(2000)  # gate+up producing the down GEMM's input
+    for rep in range(per):
+        for i in range(n):
+            add(100 + i)
+    _write_csv(str(tmp_path / "t" / "run_kernel_trace.csv"), ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    bench.trace_summary(str(tmp_path / "t"), shapes, steps, warmup)
+    out = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
+    assert len(out) == len(shapes) + 1 + n
+    assert [o["timed_avg_us"] for o in out[:2]] == [15.0, 25.0]
+    assert out[0]["avg_us"] == round((10 * per + 5 * steps) / per, 2)
+    assert out[2]["avg_us"] == 3.0 and out[2]["dispatches"] == bench.N_SMALL * bench.SMALL_REPS
+    assert [o["avg_us"] for o in out[3:]] == [100.0 + i for i in range(n)]
+    assert [o["case"] for o in out[3:]] == bench.GROUPED_CASES
+
+
+def test_packed_scale_bytes():
+    f4, b4 = bench.algo_work(64, 2112, 7168)
+    f1, b1 = bench.algo_work(64, 2112, 7168, scale_bytes=1.0)
+    kb = 7168 // 128
+    assert f1 == f4 and b4 - b1 == 3 * (64 * kb + 17 * kb)
+
+
 def test_counter_summary(tmp_path, capsys):
     shapes = [(64, 256, 512), (128, 512, 1024)]
     rows = []
-    for d in range(1, 5):
+    for d in range(1, 7):
         rows.append([d, "void fp8gemm::fp8_gemm_kernel<64, 64, 2, 2, 8, false>(fp8gemm::Params)", "GRBM_GUI_ACTIVE", 10 * d])
         rows.append([d, "void fp8gemm::fp8_gemm_kernel<64, 64, 2, 2, 8, false>(fp8gemm::Params)", "SQ_INSTS_LDS", d])
         rows.append([d, "void fp8gemm::fp8_gemm_kernel<64, 64, 2, 2, 8, false>(fp8gemm::Params)", "SQ_INSTS_LDS", d])
     _write_csv(str(tmp_path / "c" / "run_counter_collection.csv"), ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
-    bench.counter_summary(str(tmp_path / "c"), shapes)
+    bench.counter_summary(str(tmp_path / "c"), shapes, steps=1, warmup=0)
     out = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
-    # dispatches 1, 3 -> shape 0; 2, 4 -> shape 1; instances of a counter are summed per dispatch
-    assert out[0]["GRBM_GUI_ACTIVE"] == 20.0 and out[1]["GRBM_GUI_ACTIVE"] == 30.0
-    assert out[0]["SQ_INSTS_LDS"] == 4.0 and out[1]["SQ_INSTS_LDS"] == 6.0
+    # dispatches 1, 3, 5 -> shape 0; 2, 4, 6 -> shape 1; instances of a counter are summed per dispatch
+    assert out[0]["GRBM_GUI_ACTIVE"] == 30.0 and out[1]["GRBM_GUI_ACTIVE"] == 40.0
+    assert out[0]["SQ_INSTS_LDS"] == 6.0 and out[1]["SQ_INSTS_LDS"] == 8.0
 
 
 def test_multi_gpu_request_is_refused():
