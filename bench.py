@@ -474,6 +474,18 @@ def plan_sweep(args):
             c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02)
             cases.append(dict(key=[M, N, K], M=M, N=N, K=K, G=1, kind=fg.KIND_DENSE,
                               fn=(lambda c=c: fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], WS))))
+    elif args.plan_sweep == "layout":   # the TN call: both operands K-major
+        cases = []
+        for i, (M, N, K) in enumerate(CONFIG2):
+            c = synth.dense_case(M, N, K, seed=2000 + i, device=dev, a_std=1.0, b_std=0.02)
+            At = torch.zeros(K, (M + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+            At[:, :M] = c["A"].t()
+            Bt = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+            Bt[:, :N] = c["B"].t()
+            cases.append(dict(key=[M, N, K], M=M, N=N, K=K, G=1, kind=fg.KIND_LAYOUT,
+                              fn=(lambda c=c, At=At, Bt=Bt: fg.fp8_gemm_tn(At, c["sa"], Bt, c["sb"], c["D"],
+                                                                           workspace=WS))))
+            del c["A"], c["B"]
     else:
         cases = []
         for N, K in ((4096, 7168), (7168, 2048)):
@@ -483,12 +495,19 @@ def plan_sweep(args):
                                   fn=(lambda c=c: fg.fp8_grouped_gemm_nt_masked(c["A"], c["sa"], c["B"], c["sb"],
                                                                                 c["D"], c["masked_m"], 256, WS))))
     torch.cuda.synchronize()
-    tiles = [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128), (128, 256)]
+    layout = args.plan_sweep == "layout"
+    tiles = [(128, 128), (256, 256)] if layout else [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128),
+                                                      (128, 256)]
     for ti, t in enumerate(cases):
         nkb = t["K"] // 128
         masked = t["kind"] == fg.KIND_MASKED
         cands = [None]
-        for bm, bn in tiles:
+        for bm, bn in tiles if layout else ():
+            ntiles = -(-t["M"] // bm) * -(-t["N"] // bn)
+            for sp in range(1, 17):
+                if -(-nkb // -(-nkb // sp)) == sp and (sp == 1 or ntiles * sp <= 512):
+                    cands.append((bm, bn, sp, 0))
+        for bm, bn in () if layout else tiles:
             if not masked and ((t["M"] <= 128 and bm > 128) or (t["M"] > 128 and bm < 128)):
                 continue
             ntiles = -(-t["M"] // bm) * -(-t["N"] // bn)
@@ -525,7 +544,7 @@ def plan_sweep(args):
                 evs.append(ev)
             torch.cuda.synchronize()
             ms = float(np.median([a.elapsed_time(b) for a, b in evs[1:]]))
-            key = "auto" if cfg is None else ("%dx%d s%d" % cfg[:3] if masked else "%dx%d s%d f%d" % cfg)
+            key = "auto" if cfg is None else ("%dx%d s%d" % cfg[:3] if masked or layout else "%dx%d s%d f%d" % cfg)
             res[key] = round(ms * 1e3, 2)
         print(json.dumps({"kind": args.plan_sweep, "case": t["key"], "all": res}), flush=True)
 
@@ -535,8 +554,8 @@ def plan_table(args):
     into profiles/planner_sweep.json, the measured table the planner is checked against."""
     import math
     import platform
-    acc = {"dense": {}, "masked": {}}
-    runs = {"dense": 0, "masked": 0}
+    acc = {"dense": {}, "masked": {}, "layout": {}}
+    runs = {"dense": 0, "masked": 0, "layout": 0}
     for f in args.plan_table:
         with open(f) as fh:
             kinds = set()
@@ -553,10 +572,10 @@ def plan_table(args):
                 runs[k] += 1
     out = {"what": "event time (us) of every plan of each case, forced for that call only inside the benchmark's "
                    "sequence of calls; geometric mean over the runs",
-           "command": "python bench.py --plan-sweep dense --rounds 12 > LOG (twice, likewise --plan-sweep masked); "
-                      "python bench.py --plan-table LOG...",
+           "command": "python bench.py --plan-sweep dense --rounds 12 > LOG (twice, likewise --plan-sweep masked "
+                      "and layout); python bench.py --plan-table LOG...",
            "kernel_sha": kernel_source_hash(), "runs": runs}
-    for kind in ("dense", "masked"):
+    for kind in ("dense", "masked", "layout"):
         out[kind] = {case: {k: round(math.exp(sum(math.log(x) for x in v) / len(v)), 2) for k, v in tab.items()}
                      for case, tab in acc[kind].items()}
     with open(os.path.join(ROOT, "profiles", "planner_sweep.json"), "w") as fh:
@@ -790,8 +809,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--shapes", type=str, default=None, help="'M,N,K;M,N,K' instead of the default list")
-    ap.add_argument("--plan-sweep", choices=("dense", "masked"),
-                    help="time every plan of each dense shape / masked decode case (planner fitting)")
+    ap.add_argument("--plan-sweep", choices=("dense", "masked", "layout"),
+                    help="time every plan of each dense shape / masked decode case / dense shape in the TN "
+                         "layout (planner fitting)")
     ap.add_argument("--rounds", type=int, default=12, help="rounds per plan of --plan-sweep")
     ap.add_argument("--plan-table", nargs="+", metavar="LOG",
                     help="average --plan-sweep logs into profiles/planner_sweep.json")
@@ -895,14 +915,14 @@ def main():
                 Bt = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=dev)
                 Bt[:, :N] = c["B"].t()
                 c["B"] = Bt
-            big = (M + 255) // 256 * ((N + 255) // 256) >= (fg.get_num_cus() or 256)
-            c["cfg"] = {"block_m": 256 if big else 128, "block_n": 256 if big else 128, "split_k": 1}
+            c["ws"] = fg.make_workspace(fg.KIND_LAYOUT, M, N, K, device=dev)
+            c["cfg"] = fg.query_config(fg.KIND_LAYOUT, M, N, K)
         cases.append(c)
     torch.cuda.synchronize()
 
     def call(c):
         if tn:
-            getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"], ue8m0=ue8m0)
+            getattr(fg, layout_fn)(c["A"], c["sa"], c["B"], c["sb"], c["D"], ue8m0=ue8m0, workspace=c["ws"])
         elif c["C"] is not None:
             fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], c["D"], c["ws"], C=c["C"])
         else:

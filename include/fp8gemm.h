@@ -45,8 +45,8 @@
  *    argument error nothing is launched. No exception crosses the ABI.
  *  - Preconditions on device data (cannot be checked from the host): no e4m3 NaN
  *    codes in live rows; m_indices / masked_m as documented per call.
- *  - Split-K workspace: optional. When `workspace` is NULL or smaller than
- *    fp8_gemm_workspace_size(...), the call runs without split-K (or with fewer
+ *  - Split-K workspace: optional, 16-byte aligned. When `workspace` is NULL or smaller
+ *    than fp8_gemm_workspace_size(...), the call runs without split-K (or with fewer
  *    split tiles). Layout: the first 16 KiB hold 4096 int32 arrival counters, the
  *    rest FP32 partial sums. The counters must be zero before the workspace's first
  *    use (zero-fill the buffer once); every call that completes leaves them zero
@@ -76,7 +76,10 @@ enum {
   FP8GEMM_ERR_CONFIG = -7     /* an invalid forced tile configuration                */
 };
 
-enum { FP8GEMM_KIND_DENSE = 0, FP8GEMM_KIND_CONTIGUOUS = 1, FP8GEMM_KIND_MASKED = 2 };
+/* Call kinds of the planner queries (fp8_gemm_workspace_size, fp8_gemm_query_config):
+ * the dense NT call, the two M-grouped calls, and the dense TN / NN / TT calls, which
+ * share one plan. */
+enum { FP8GEMM_KIND_DENSE = 0, FP8GEMM_KIND_CONTIGUOUS = 1, FP8GEMM_KIND_MASKED = 2, FP8GEMM_KIND_LAYOUT = 3 };
 
 /* Tile configuration chosen for (or forced on) a call. */
 typedef struct {
@@ -305,11 +308,15 @@ int fp8_grouped_gemm_nt_masked_ue8m0(const void* A, int64_t lda, const float* sa
  *   D   BF16 [M][ldd], ldd >= N, 2-byte aligned (8-byte stores when ldd % 4 == 0 and D
  *       is 8-byte aligned).
  * M >= 0 (0: nothing to do), N > 0, K > 0 and a multiple of 128. Errors as for
- * fp8_gemm_nt; the call needs no workspace.
+ * fp8_gemm_nt. workspace / workspace_bytes: the optional split-K workspace of the
+ * conventions above, sized by fp8_gemm_workspace_size(FP8GEMM_KIND_LAYOUT, M, N, K, 1,
+ * 0); the TN, NN and TT calls split K when their tiles would leave most CUs idle (the
+ * few-row shapes).
  */
 int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 const void* B, int64_t ldb, const float* sb,
-                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                void* D, int64_t ldd, int M, int N, int K,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The dense call in the NN and TT layouts (es.news.hada.io/topic?id=19459, "Interfaz
@@ -322,10 +329,12 @@ int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
  */
 int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 const void* B, int64_t ldb, const float* sb,
-                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                void* D, int64_t ldd, int M, int N, int K,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                 const void* B, int64_t ldb, const float* sb,
-                void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                void* D, int64_t ldd, int M, int N, int K,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The TN, NN and TT calls in the accumulate form D = C + A B (the pages' naming of every
@@ -338,13 +347,16 @@ int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
  */
 int fp8_gemm_tn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                   const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
-                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                  void* D, int64_t ldd, int M, int N, int K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fp8_gemm_nn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                   const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
-                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                  void* D, int64_t ldd, int M, int N, int K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                   const void* B, int64_t ldb, const float* sb, const void* C, int64_t ldc,
-                  void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                  void* D, int64_t ldd, int M, int N, int K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The TN, NN and TT calls with UE8M0 scale factors (both from es.news.hada.io/topic?
@@ -354,13 +366,16 @@ int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
  */
 int fp8_gemm_tn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const void* B, int64_t ldb, const float* sb,
-                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                      void* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fp8_gemm_nn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const void* B, int64_t ldb, const float* sb,
-                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                      void* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fp8_gemm_tt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const void* B, int64_t ldb, const float* sb,
-                      void* D, int64_t ldd, int M, int N, int K, hipStream_t stream);
+                      void* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * K-grouped TN GEMM, the MoE weight-gradient form: grouping along K with M and N
@@ -462,12 +477,12 @@ int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int
 /* Bytes of split-K workspace the call with these sizes may use (0 = never splits).
  * Splitting K is this library's choice for MI355X (the pages' Hopper kernels do not
  * split K), so this utility has no counterpart on the pages.
- * kind: FP8GEMM_KIND_*. M is M (dense), M_total (contiguous) or M_max (masked).
- * expected_m is the masked call's tiling hint, taken here so that the answer is
- * computed by the same planner with the same arguments as the call itself (the
- * masked call never splits K today, so it returns 0 for FP8GEMM_KIND_MASKED; the
- * argument is ignored for the other kinds). The size includes the 16 KiB counter
- * block described in the conventions above. */
+ * kind: FP8GEMM_KIND_*. M is M (dense, layout), M_total (contiguous) or M_max
+ * (masked). expected_m is the masked call's tiling hint, taken here so that the answer
+ * is computed by the same planner with the same arguments as the call itself (the
+ * masked workspace holds the live tiles of up to twice expected_m rows per group); it
+ * is ignored for the other kinds. The size includes the 16 KiB counter block
+ * described in the conventions above. */
 size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expected_m);
 
 /* Configuration the library would use for a call (no launch, no device access
@@ -483,8 +498,11 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m,
  * block_n, split_k and full_tiles (clamped to the tile count; 0 splits every
  * tile) are used, grid and num_units are ignored. NULL restores
  * automatic selection. Not thread-safe; process-wide.
- * Returns FP8GEMM_ERR_CONFIG for a tile shape that has no kernel; a later call
- * returns FP8GEMM_ERR_CONFIG if the forced plan splits more than 4096 tiles. */
+ * Returns FP8GEMM_ERR_CONFIG for a tile shape that no call has a kernel for; a later
+ * call returns FP8GEMM_ERR_CONFIG if it has no kernel for the forced tile (the NT and
+ * M-grouped calls: 64x64, 128x64, 64x128, 128x128, 256x128, 128x256; the TN / NN / TT
+ * calls: 128x128, 256x256, which ignore full_tiles) or if the forced plan splits more
+ * than 4096 tiles. */
 int fp8_gemm_force_config(const fp8gemm_config_t* cfg);
 
 /* Cap on the compute units the persistent grid is sized for: the analog of

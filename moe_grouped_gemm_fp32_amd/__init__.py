@@ -27,12 +27,12 @@ __all__ = [
     "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "noalloc_scratch_bytes", "fp8_gemm_nt_ue8m0", "fp8_grouped_gemm_nt_contiguous", "fp8_grouped_gemm_nt_masked",
     "workspace_size", "make_workspace", "query_config", "force_config", "set_num_cus",
     "get_num_cus", "get_mk_alignment_for_contiguous_layout", "scale_ld", "num_tiles",
-    "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED", "quantize_1x128",
+    "status_string", "lib", "LIB_PATH", "KIND_DENSE", "KIND_CONTIGUOUS", "KIND_MASKED", "KIND_LAYOUT", "quantize_1x128",
     "Fp8GemmError",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8gemm.so")
-KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED = 0, 1, 2
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_LAYOUT = 0, 1, 2, 3
 
 
 class Fp8GemmError(RuntimeError):
@@ -66,15 +66,15 @@ _SIGS = {
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_grouped_gemm_nt_masked_ue8m0": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
-    "fp8_gemm_tn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_nn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_tt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_tn_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_nn_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_tt_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_tn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_nn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
-    "fp8_gemm_tt_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P]),
+    "fp8_gemm_tn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_nn": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tt": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tn_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_nn_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tt_c": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_nn_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
+    "fp8_gemm_tt_ue8m0": (_INT, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _INT, _INT, _INT, _P, _SZ, _P]),
     "fp8_k_grouped_gemm_tn_contiguous": (
         _INT, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _INT, _INT, _INT, _INT, _P]),
     "fp8_k_grouped_gemm_tn_contiguous_ue8m0": (
@@ -483,7 +483,7 @@ def fp8_grouped_gemm_nt_masked(A, sa, B, sb, D, masked_m, expected_m: int, works
     return D
 
 
-def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream, C=None):
+def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream, C=None, workspace=None):
     A, B = _bytes_view(A), _bytes_view(B)
     dev = D.device
     _require(dev.type == "cuda" and all(t.device == dev for t in (A, sa, B, sb)), "tensors must share one GPU")
@@ -499,39 +499,44 @@ def _dense_layout(name, a_kmajor, b_kmajor, A, sa, B, sb, D, stream, C=None):
              "sa must be float32 [K/128, >=M]")
     _require(sb.dtype == torch.float32 and sb.is_contiguous() and sb.numel() == ((N + 127) // 128) * (K // 128),
              "sb must be contiguous float32 [ceil(N/128), K/128]")
+    wp, wb = _ws(workspace)
     if C is not None:
         _check_c(C, D)
         name = name + "_c"
         st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
-                                  _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
+                                  _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     else:
         st = getattr(lib(), name)(_ptr(A), A.stride(0), _ptr(sa), _ld(sa), _ptr(B), B.stride(0), _ptr(sb),
-                                  _ptr(D), D.stride(0), M, N, K, _stream(dev, stream))
+                                  _ptr(D), D.stride(0), M, N, K, wp, wb, _stream(dev, stream))
     _check(st, name)
     return D
 
 
 def fp8_gemm_tn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
-                ue8m0: bool = False, C: Optional[torch.Tensor] = None):
+                ue8m0: bool = False, C: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense TN GEMM: D [M, N] (bfloat16) = A^T B with A [K, M] and B [K, N] (e4m3 bytes,
     K-major, unit inner stride), sa [K/128, >=M] and sb [ceil(N/128), K/128] as for
-    fp8_gemm_nt."""
+    fp8_gemm_nt. workspace: optional split-K workspace (make_workspace(KIND_LAYOUT, M, N,
+    K)), used by the few-row shapes."""
     _require(not (ue8m0 and C is not None), "the UE8M0 form takes no C")
-    return _dense_layout("fp8_gemm_tn" + ("_ue8m0" if ue8m0 else ""), True, True, A, sa, B, sb, D, stream, C)
+    return _dense_layout("fp8_gemm_tn" + ("_ue8m0" if ue8m0 else ""), True, True, A, sa, B, sb, D, stream, C,
+                         workspace)
 
 
 def fp8_gemm_nn(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
-                ue8m0: bool = False, C: Optional[torch.Tensor] = None):
+                ue8m0: bool = False, C: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense NN GEMM: D = A B with A [M, K] (as for fp8_gemm_nt) and B [K, N] (K-major)."""
     _require(not (ue8m0 and C is not None), "the UE8M0 form takes no C")
-    return _dense_layout("fp8_gemm_nn" + ("_ue8m0" if ue8m0 else ""), False, True, A, sa, B, sb, D, stream, C)
+    return _dense_layout("fp8_gemm_nn" + ("_ue8m0" if ue8m0 else ""), False, True, A, sa, B, sb, D, stream, C,
+                         workspace)
 
 
 def fp8_gemm_tt(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor, stream=None,
-                ue8m0: bool = False, C: Optional[torch.Tensor] = None):
+                ue8m0: bool = False, C: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense TT GEMM: D = A^T B^T with A [K, M] (K-major) and B [N, K] (as for fp8_gemm_nt)."""
     _require(not (ue8m0 and C is not None), "the UE8M0 form takes no C")
-    return _dense_layout("fp8_gemm_tt" + ("_ue8m0" if ue8m0 else ""), True, False, A, sa, B, sb, D, stream, C)
+    return _dense_layout("fp8_gemm_tt" + ("_ue8m0" if ue8m0 else ""), True, False, A, sa, B, sb, D, stream, C,
+                         workspace)
 
 
 MAX_K_GROUPS = 256  # groups per fp8_k_grouped_gemm_tn_contiguous call

@@ -373,6 +373,7 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   int st;
   const int cus = effective_cus(true, &st);
   if (st != FP8GEMM_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return FP8GEMM_ERR_LAYOUT;
   const size_t ws_avail = workspace ? workspace_bytes : 0;
   Plan pl = choose(kind, rows, N, K, G, expected_m, cus, ws_avail);
   if (!has_kernel(pl.bm, pl.bn)) return FP8GEMM_ERR_CONFIG;
@@ -723,32 +724,91 @@ int fp8_k_grouped_gemm_tn_contiguous_ue8m0(const void* A, int64_t lda, const flo
 }  // extern "C"
 
 namespace {
+// Tile plans of the dense layout calls (TN, NN, TT). Instances: 256x256 tiles (8 waves of
+// 64x128, a 2-stage ring); 128x128 tiles (4 waves of 64x64) with a 2-stage ring, of
+// which two workgroups share a CU, or a 4-stage ring (one workgroup per CU, more bytes
+// in flight per unit) for plans whose units all run in one round.
+struct LayoutPlan {
+  int bm = 128, bn = 128, split = 1, kbps = 0, stages = 2;
+  int64_t tiles = 0, units = 0;
+  size_t ws_bytes = 0;
+};
+
+bool is_layout_tile(int bm, int bn) { return (bm == 128 && bn == 128) || (bm == 256 && bn == 256); }
+
+// 256x256 tiles once they alone give every CU a tile. Otherwise 128x128 tiles; when
+// those leave CUs idle, K is split as far as all units still run in one round and the
+// workspace holds the partials, choosing the split by a cost model fitted to measured
+// timings of every split of the few-row shapes (bench.py --plan-sweep layout): a unit
+// takes kLayoutKbUs per K block and the last arrival kLayoutSplitUs per further split
+// (publishing, arrival and reading a partial).
+constexpr int kLayoutMaxSplit = 16;
+constexpr double kLayoutKbUs = 0.9;
+constexpr double kLayoutSplitUs = 1.0;
+LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
+  LayoutPlan pl;
+  const int num_kb = K / fp8gemm::kBlockK;
+  if (g_forced) {
+    pl.bm = g_forced_cfg.block_m;
+    pl.bn = g_forced_cfg.block_n;
+    pl.split = std::max(1, std::min(g_forced_cfg.split_k, num_kb));
+  } else if (ceil_div(M, 256) * ceil_div(N, 256) >= cus) {
+    pl.bm = pl.bn = 256;
+  } else {
+    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    double best = 1e30;
+    for (int sp = 1; sp <= std::min(num_kb, kLayoutMaxSplit); ++sp) {
+      const int kbps = (int)ceil_div(num_kb, sp);
+      if (ceil_div(num_kb, kbps) != sp) continue;  // the same as a smaller split
+      if (sp > 1 && (tiles * sp > cus || tiles > kMaxSplitTiles || split_ws_bytes(tiles, sp, 128, 128) > ws_avail))
+        continue;
+      const double t = kbps * kLayoutKbUs + (sp - 1) * kLayoutSplitUs;
+      if (t < best) {
+        best = t;
+        pl.split = sp;
+      }
+    }
+  }
+  pl.kbps = (int)ceil_div(num_kb, pl.split);
+  pl.split = (int)ceil_div(num_kb, pl.kbps);  // no empty splits
+  pl.tiles = ceil_div(M, pl.bm) * ceil_div(N, pl.bn);
+  pl.units = pl.tiles * pl.split;
+  pl.ws_bytes = split_ws_bytes(pl.tiles, pl.split, pl.bm, pl.bn);
+  pl.stages = (pl.bm == 128 && pl.units <= cus) ? 4 : 2;
+  return pl;
+}
+
 template <bool E8, bool A_KC, bool B_KC>
-void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hipStream_t stream) {
-  if (big)
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, E8, true, A_KC, B_KC>), dim3((unsigned)tiles),
-                       dim3(512), 0, stream, p);
+void launch_dense_layout(const fp8gemm::KParams& p, const LayoutPlan& pl, hipStream_t stream) {
+  const dim3 grid((unsigned)pl.units);
+  if (pl.bm == 256)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, E8, true, A_KC, B_KC>), grid, dim3(512), 0,
+                       stream, p);
+  else if (pl.stages == 4)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 4, E8, true, A_KC, B_KC>), grid, dim3(256), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, E8, true, A_KC, B_KC>), dim3((unsigned)tiles),
-                       dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 2, E8, true, A_KC, B_KC>), grid, dim3(256), 0,
+                       stream, p);
 }
 template <bool E8>
-void launch_dense_layout(const fp8gemm::KParams& p, bool big, int64_t tiles, hipStream_t stream, bool a_kc,
+void launch_dense_layout(const fp8gemm::KParams& p, const LayoutPlan& pl, hipStream_t stream, bool a_kc,
                          bool b_kc) {
   if (a_kc)
-    launch_dense_layout<E8, true, false>(p, big, tiles, stream);
+    launch_dense_layout<E8, true, false>(p, pl, stream);
   else if (b_kc)
-    launch_dense_layout<E8, false, true>(p, big, tiles, stream);
+    launch_dense_layout<E8, false, true>(p, pl, stream);
   else
-    launch_dense_layout<E8, false, false>(p, big, tiles, stream);
+    launch_dense_layout<E8, false, false>(p, pl, stream);
 }
 
 // The dense call in the TN (a_kc = b_kc = false), NN (a_kc) and TT (b_kc) layouts: a
 // K-contiguous operand is [rows][ld >= K], a K-major one [K][ld >= rows]. e8: UE8M0
 // (power-of-two) scales applied by the block-scaled MFMA.
 int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                 const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream, bool a_kc,
-                 bool b_kc, bool e8 = false, const void* C = nullptr, int64_t ldc = 0) {
+                 const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream, bool a_kc, bool b_kc, bool e8 = false,
+                 const void* C = nullptr, int64_t ldc = 0) {
   if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL;
   if (M < 0 || N <= 0 || K <= 0 || K % fp8gemm::kBlockK != 0) return FP8GEMM_ERR_SHAPE;
   // 16-byte row chunks; 128 rows of either operand addressed with 32-bit lane offsets
@@ -759,10 +819,17 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(D, 2))
     return FP8GEMM_ERR_LAYOUT;
   if (C && (ldc < N || !aligned(C, 2))) return FP8GEMM_ERR_LAYOUT;
+  if (workspace && !aligned(workspace, 16)) return FP8GEMM_ERR_LAYOUT;
   int st;
   const int cus = effective_cus(true, &st);
   if (st != FP8GEMM_OK) return st;
+  if (g_forced && !is_layout_tile(g_forced_cfg.block_m, g_forced_cfg.block_n)) return FP8GEMM_ERR_CONFIG;
   if (M == 0) return FP8GEMM_OK;
+  const size_t ws_avail = workspace ? workspace_bytes : 0;
+  const LayoutPlan pl = choose_layout(M, N, K, cus, ws_avail);
+  if (pl.split > 1 && pl.tiles > kMaxSplitTiles) return FP8GEMM_ERR_CONFIG;
+  if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
+  if (pl.units > INT32_MAX) return FP8GEMM_ERR_SHAPE;
   fp8gemm::KParams p{};
   p.C = static_cast<const uint16_t*>(C);
   p.ldc = ldc;
@@ -777,16 +844,18 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   p.kb_start[0] = 0;
   p.kb_start[1] = K / fp8gemm::kBlockK;
   p.vec4 = (ldd % 4 == 0 && aligned(D, 8)) ? 1 : 0;
-  // the tile rule of the K-grouped call
-  const bool big = ceil_div(M, 256) * ceil_div(N, 256) >= cus;
-  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
-  p.tiles_m = (int)ceil_div(M, bm);
-  p.tiles_n = (int)ceil_div(N, bn);
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.tiles_m = (int)ceil_div(M, pl.bm);
+  p.tiles_n = (int)ceil_div(N, pl.bn);
+  p.split_k = pl.split;
+  p.kb_per_split = pl.kbps;
+  if (pl.split > 1) {
+    p.counters = static_cast<int32_t*>(workspace);
+    p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+  }
   if (e8)
-    launch_dense_layout<true>(p, big, tiles, stream, a_kc, b_kc);
+    launch_dense_layout<true>(p, pl, stream, a_kc, b_kc);
   else
-    launch_dense_layout<false>(p, big, tiles, stream, a_kc, b_kc);
+    launch_dense_layout<false>(p, pl, stream, a_kc, b_kc);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_ERR_LAUNCH;
 }
 }  // namespace
@@ -794,54 +863,69 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
 extern "C" {
 
 int fp8_gemm_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false);
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      false);
 }
 
 int fp8_gemm_nn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false);
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, true,
+                      false);
 }
 
 int fp8_gemm_tt(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true);
+                const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      true);
 }
 
 int fp8_gemm_tn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                   const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
-                  hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!C) return FP8GEMM_ERR_NULL;
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false, false, C, ldc);
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      false, false, C, ldc);
 }
 
 int fp8_gemm_nn_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                   const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
-                  hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!C) return FP8GEMM_ERR_NULL;
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false, false, C, ldc);
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, true,
+                      false, false, C, ldc);
 }
 
 int fp8_gemm_tt_c(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
                   const float* sb, const void* C, int64_t ldc, void* D, int64_t ldd, int M, int N, int K,
-                  hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!C) return FP8GEMM_ERR_NULL;
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true, false, C, ldc);
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      true, false, C, ldc);
 }
 
 int fp8_gemm_tn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, false, true);
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      false, true);
 }
 
 int fp8_gemm_nn_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, true, false, true);
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, true,
+                      false, true);
 }
 
 int fp8_gemm_tt_ue8m0(const void* A, int64_t lda, const float* sa, int64_t ld_sa, const void* B, int64_t ldb,
-                      const float* sb, void* D, int64_t ldd, int M, int N, int K, hipStream_t stream) {
-  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, false, true, true);
+                      const float* sb, void* D, int64_t ldd, int M, int N, int K, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return dense_layout(A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace, workspace_bytes, stream, false,
+                      true, true);
 }
 
 int fp8_swiglu_quantize_1x128(const void* H, int64_t ldh, int h_dtype, const int32_t* m_indices, void* Q,
@@ -894,6 +978,10 @@ size_t fp8_gemm_workspace_size(int kind, int M, int N, int K, int G, int expecte
   if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
   int st;
   const int cus = effective_cus(false, &st);
+  if (kind == FP8GEMM_KIND_LAYOUT) {
+    const LayoutPlan pl = choose_layout(M, N, K, cus, SIZE_MAX);
+    return pl.split > 1 ? pl.ws_bytes : 0;
+  }
   const Plan pl = choose(kind, M, N, K, std::max(G, 1), expected_m, cus, SIZE_MAX);
   return pl.split > 1 ? pl.ws_bytes : 0;
 }
@@ -904,6 +992,16 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m, 
   if (M < 0 || N <= 0 || K <= 0 || K % 128 || G <= 0) return FP8GEMM_ERR_SHAPE;
   int st;
   const int cus = effective_cus(false, &st);
+  if (kind == FP8GEMM_KIND_LAYOUT) {
+    const LayoutPlan pl = choose_layout(M, N, K, cus, workspace_bytes);
+    out->block_m = pl.bm;
+    out->block_n = pl.bn;
+    out->split_k = pl.split;
+    out->grid = (int)pl.units;
+    out->num_units = (int)pl.units;
+    out->full_tiles = pl.split > 1 ? 0 : (int)pl.tiles;
+    return FP8GEMM_OK;
+  }
   const Plan pl = choose(kind, M, N, K, G, expected_m, cus, workspace_bytes);
   out->block_m = pl.bm;
   out->block_n = pl.bn;
@@ -919,7 +1017,8 @@ int fp8_gemm_force_config(const fp8gemm_config_t* cfg) {
     g_forced = false;
     return FP8GEMM_OK;
   }
-  if (!has_kernel(cfg->block_m, cfg->block_n) || cfg->split_k < 1) return FP8GEMM_ERR_CONFIG;
+  if (!(has_kernel(cfg->block_m, cfg->block_n) || is_layout_tile(cfg->block_m, cfg->block_n)) || cfg->split_k < 1)
+    return FP8GEMM_ERR_CONFIG;
   g_forced_cfg = *cfg;
   g_forced = true;
   return FP8GEMM_OK;

@@ -257,25 +257,30 @@ __device__ __forceinline__ void wait_stages(int n) {
 // Partials move as device-coherent (sc1) 16-byte buffer accesses, one kilobyte of
 // contiguous lines per instruction; the last arrival issues all loads of a partial
 // before adding any of them, so each partial costs one round trip.
+// ws: the partials [split tile][S][tile_floats]; counters: one per split tile.
+// live_t (wave-uniform): only the fragments of rows t < live_t hold output rows, the
+// others lie past M; they are neither published nor read (their sums are never stored).
 template <int TM, int TN>
-__device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN], int ws_id, int split, int S,
-                                              int frag_base, int tile_floats, int tid, int* s_flag) {
+__device__ __forceinline__ bool reduce_splits(float* ws, int32_t* counters, v4f (&acc)[TM][TN], int ws_id,
+                                              int split, int S, int frag_base, int tile_floats, int tid,
+                                              int* s_flag, int live_t = TM) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   constexpr int kDeviceScope = 16;       // buffer cache policy: sc1
   constexpr int kRawDword3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, untyped access
-  float* tile_ws = const_cast<float*>(uni((const float*)(p.ws + (int64_t)ws_id * S * tile_floats)));
+  float* tile_ws = const_cast<float*>(uni((const float*)(ws + (int64_t)ws_id * S * tile_floats)));
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tile_ws, 0, S * tile_floats * 4, kRawDword3);
   auto offset = [&](int q, int t, int j) { return (q * tile_floats + (frag_base + (t * TN + j) * 64) * 4) * 4; };
 #pragma unroll
   for (int t = 0; t < TM; ++t)
+    if (t < live_t)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[t][j]), rs, offset(split, t, j), 0,
-                                             kDeviceScope);
+      for (int j = 0; j < TN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[t][j]), rs, offset(split, t, j), 0,
+                                               kDeviceScope);
   wait_vmcnt<0>();  // the partial has reached the device-coherent level
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&p.counters[ws_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(&counters[ws_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = (old == S - 1);
   }
   __syncthreads();
@@ -299,7 +304,9 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
       for (int t = 0; t < TM; ++t)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          part[t][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, offset(q, t, j), 0, kDeviceScope));
+          part[t][j] = t < live_t ? __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                rs, offset(q, t, j), 0, kDeviceScope))
+                                  : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -310,7 +317,7 @@ __device__ __forceinline__ bool reduce_splits(const Params& p, v4f (&acc)[TM][TN
   for (int t = 0; t < TM; ++t)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[t][j] = sum[t][j];
-  if (tid == 0) __hip_atomic_store(&p.counters[ws_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&counters[ws_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -803,7 +810,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     }
 
     // ---- split-K: the last of the S arrivals writes the tile
-    if (S_u > 1 && !reduce_splits(p, acc, ws_id, split, S_u, (wave * TM * TN) * 64 + lane, BM * BN, tid, &s_info))
+    if (S_u > 1 && !reduce_splits(p.ws, p.counters, acc, ws_id, split, S_u, (wave * TM * TN) * 64 + lane, BM * BN, tid, &s_info))
       continue;
 
     // ---- epilogue: BF16 round-to-nearest-even, live rows only; subtiles 2h and 2h+1

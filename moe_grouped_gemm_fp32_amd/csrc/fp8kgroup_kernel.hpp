@@ -52,6 +52,11 @@ struct KParams {
   int tiles_m, tiles_n;
   int accumulate;  // 1: D += result, 0: D = result
   int vec4;        // 1: D rows allow 16-byte accesses (ldd % 4 == 0, D 16-byte aligned)
+  // split-K of the dense layout calls: each tile is split_k units of kb_per_split K
+  // blocks (the last may be shorter); partials and arrival counters as in the NT call
+  int split_k, kb_per_split;
+  float* ws;
+  int32_t* counters;
   int kb_start[kMaxKGroups + 1];  // group g covers K blocks [kb_start[g], kb_start[g+1])
 };
 
@@ -79,7 +84,10 @@ __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >>
 // DENSE_TN instances are the dense call in another memory layout (one group over all of
 // K): B carries one scale per 128x128 block (sb [ceil(N/128)][ld_sb = K/128]) as in the NT
 // call, and the output is BF16 (round to nearest even once, from the FP32 accumulator,
-// after adding the optional BF16 C of D = C + A B).
+// after adding the optional BF16 C of D = C + A B). They may split K: the grid is then
+// split_k units per tile, numbered split-major (the units that read the same K range of
+// A run next to each other, on one XCD), and the last arrival of a tile's units sums the
+// FP32 partials in split order before the epilogue, as in the NT kernel.
 // A_KC / B_KC make that operand K-contiguous ([rows][K], as in the NT call) instead of
 // K-major: its panels hold [128 rows][128 k] in the NT kernel's swizzled row layout and
 // its fragments come from two 16-byte reads per lane, with the same lane -> K order as
@@ -105,14 +113,19 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   const int wave = uni(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // tile of this workgroup: XCD-contiguous ranges of a group-major, rasterised order
+  // tile of this workgroup: XCD-contiguous ranges of a group-major (K-grouped) or
+  // split-major (dense layouts) rasterised order
   const int per_group = p.tiles_m * p.tiles_n;
-  const int L = xcd_remap(blockIdx.x, p.G * per_group);
-  const int g = L / per_group;
+  const int S = DENSE_TN ? p.split_k : 1;
+  const int L = xcd_remap(blockIdx.x, p.G * per_group * S);
+  const int g = DENSE_TN ? 0 : L / per_group;
+  const int split = DENSE_TN ? L / per_group : 0;
+  const int tile = L - (g + split) * per_group;
   int tm, tn;
-  raster(L - g * per_group, p.tiles_m, p.tiles_n, 8, tm, tn);
+  raster(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kb0 = p.kb_start[g], nkb = p.kb_start[g + 1] - kb0;
+  const int kb0 = p.kb_start[g] + split * p.kb_per_split;
+  const int nkb = S > 1 ? min(p.kb_per_split, p.kb_start[g + 1] - kb0) : p.kb_start[g + 1] - kb0;
 
   // ---- direct-to-LDS load plan (the same per-lane offsets for every K block). Panel load
   // u = LPW wave + i covers rows 8 (u % 16) + lane / 8 of panel u / 16 (A panels first),
@@ -271,6 +284,13 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
 
   // ---- epilogue: lane holds D[m][n .. n + 3] of each fragment
   if constexpr (DENSE_TN) {
+    __shared__ int s_last;
+    // fragments of this wave whose rows start below M (the few-row shapes leave whole
+    // fragments past M)
+    const int live_t = max(0, min(4, (p.M - m0 - 64 * wm + 15) >> 4));
+    if (S > 1 && !reduce_splits(p.ws, p.counters, acc, tile, split, S, (wave * 4 * TNW) * 64 + lane, BM * BN, tid,
+                                &s_last, live_t))
+      return;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int m = m0 + 64 * wm + 16 * t + li;

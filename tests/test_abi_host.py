@@ -239,20 +239,59 @@ def test_layout_argument_validation_without_launch(name, a_kc, b_kc):
     M, N, K = 4096, 7168, 2048
     fn = getattr(fg.lib(), name)
     base = dict(A=1 << 20, lda=K if a_kc else M, sa=1 << 20, ld_sa=M, B=1 << 20, ldb=K if b_kc else N,
-                sb=1 << 20, D=1 << 20, ldd=N, M=M, N=N, K=K)
+                sb=1 << 20, D=1 << 20, ldd=N, M=M, N=N, K=K, ws=0, wsb=0)
 
     def call(**kw):
         a = dict(base, **kw)
         return fn(P(a["A"]), a["lda"], P(a["sa"]), a["ld_sa"], P(a["B"]), a["ldb"], P(a["sb"]), P(a["D"]), a["ldd"],
-                  a["M"], a["N"], a["K"], None)
+                  a["M"], a["N"], a["K"], P(a["ws"]) if a["ws"] else None, a["wsb"], None)
 
     assert call(A=0) == -1 and call(sb=0) == -1 and call(D=0) == -1
     assert call(K=100) == -2 and call(N=0) == -2 and call(M=-1) == -2
     assert call(lda=(K if a_kc else M) - 16) == -3 and call(ldb=(K if b_kc else N) + 8) == -3
     assert call(ld_sa=M - 4) == -3 and call(ldd=N - 1) == -3 and call(A=(1 << 20) + 8) == -3
+    assert call(ws=(1 << 20) + 8, wsb=1 << 20) == -3   # the workspace is 16-byte aligned
     import torch
     if not torch.cuda.is_available():
         assert call() == -5   # valid: stops at the device check
+
+
+def test_layout_planner_splits_few_row_shapes():
+    """The TN / NN / TT plan: 256x256 tiles when they fill the CUs, 128x128 otherwise;
+    K split (at least two K blocks a unit) when the 128x128 tiles leave more than half the
+    CUs idle and the workspace holds the partials; no split without a workspace."""
+    fg.set_num_cus(256)
+    try:
+        L = fg.KIND_LAYOUT
+        big = fg.query_config(L, 4096, 7168, 16384)
+        assert (big["block_m"], big["block_n"], big["split_k"]) == (256, 256, 1)
+        assert fg.workspace_size(L, 4096, 7168, 16384) == 0
+        mid = fg.query_config(L, 4096, 2112, 7168)     # 544 tiles of 128x128
+        assert (mid["block_m"], mid["split_k"]) == (128, 1)
+        for M, N, K in [(64, 2112, 7168), (128, 7168, 2048), (128, 4096, 7168)]:
+            cfg = fg.query_config(L, M, N, K)
+            tiles = fg.num_tiles(M, N, 128, 128)
+            assert cfg["block_m"] == 128 and cfg["split_k"] > 1
+            assert cfg["num_units"] == tiles * cfg["split_k"] <= 256
+            kbps = -(-(K // 128) // cfg["split_k"])
+            assert kbps >= 2 and -(-(K // 128) // kbps) == cfg["split_k"]   # no empty split
+            ws = fg.workspace_size(L, M, N, K)
+            assert ws == 16384 + tiles * cfg["split_k"] * 128 * 128 * 4
+            assert fg.query_config(L, M, N, K, workspace_bytes=ws) == cfg
+            assert fg.query_config(L, M, N, K, workspace_bytes=0)["split_k"] == 1
+        # a workspace too small for the chosen split falls back to a smaller one
+        M, N, K = 64, 2112, 7168
+        cfg = fg.query_config(L, M, N, K)
+        small = fg.query_config(L, M, N, K, workspace_bytes=fg.workspace_size(L, M, N, K) // 2)
+        assert 1 < small["split_k"] < cfg["split_k"]
+        with fg.force_config(256, 256, 3):
+            f = fg.query_config(L, 64, 2112, 7168)
+            assert (f["block_m"], f["split_k"]) == (256, 3)
+    finally:
+        fg.set_num_cus(0)
+    with pytest.raises(fg.Fp8GemmError):
+        with fg.force_config(256, 64):
+            pass
 
 
 def test_swiglu_quantize_argument_validation_without_launch():

@@ -84,16 +84,18 @@ def test_split_k_is_deterministic_and_workspace_self_resets(cuda_device):
 
 @pytest.mark.parametrize("order", [0, 1])
 def test_one_workspace_shared_by_different_split_plans(cuda_device, order):
-    """Two shapes whose plans differ (tile, split count and number of split tiles) run one
-    after the other through one workspace, in both orders, twice: the counters sit at a
-    fixed place, so neither call sees the other's partials as counters."""
-    shapes = [(64, 2112, 7168), (64, 7168, 2048), (128, 2112, 7168)]
+    """Shapes whose plans differ (tile, split count and number of split tiles) run one
+    after the other through one workspace, in both orders, twice, with a TN-layout call
+    (its own tiles and split) among them: the counters sit at a fixed place, so no call
+    sees another's partials as counters."""
+    shapes = [(64, 2112, 7168), (64, 4096, 7168), (128, 2112, 7168), (64, 7168, 2048)]
+    kinds = [fg.KIND_DENSE, fg.KIND_DENSE, fg.KIND_DENSE, fg.KIND_LAYOUT]
     if order:
-        shapes = shapes[::-1]
-    plans = [fg.query_config(fg.KIND_DENSE, *s) for s in shapes]
+        shapes, kinds = shapes[::-1], kinds[::-1]
+    plans = [fg.query_config(k, *s) for k, s in zip(kinds, shapes)]
     assert all(p["split_k"] > 1 for p in plans), plans
     assert len({(p["block_m"], p["block_n"], p["split_k"], p["num_units"]) for p in plans}) == len(plans)
-    nbytes = max(fg.workspace_size(fg.KIND_DENSE, *s) for s in shapes)
+    nbytes = max(fg.workspace_size(k, *s) for k, s in zip(kinds, shapes))
     work = torch.zeros(nbytes, dtype=torch.uint8, device=cuda_device)
     cases = [synth.dense_case(M, N, K, seed=4100 + i, device=cuda_device, a_std=1.0, b_std=0.02)
              for i, (M, N, K) in enumerate(shapes)]
@@ -102,9 +104,15 @@ def test_one_workspace_shared_by_different_split_plans(cuda_device, order):
         rows = sample_rows(M, 10, N + K)
         refs.append((rows, oracle.gemm_nt_sampled(*host(c, "A", "sa", "B", "sb"), rows, np.arange(N))[0]))
     for rep in range(2):
-        for (M, N, K), c, (rows, ref) in zip(shapes, cases, refs):
+        for (M, N, K), kind, c, (rows, ref) in zip(shapes, kinds, cases, refs):
             D = c["D"].clone()
-            fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
+            if kind == fg.KIND_LAYOUT:   # the same product with both operands stored K-major
+                At = c["A"].t().contiguous()
+                Bt = torch.zeros(K, (N + 15) // 16 * 16, dtype=torch.uint8, device=cuda_device)
+                Bt[:, :N] = c["B"].t()
+                fg.fp8_gemm_tn(At, c["sa"], Bt, c["sb"], D, workspace=work)
+            else:
+                fg.fp8_gemm_nt(c["A"], c["sa"], c["B"], c["sb"], D, work)
             torch.cuda.synchronize()
             bits = bits_of(D)
             assert not np.any(bits == SENT), f"{M}x{N}x{K} pass {rep}: an output tile was not written"

@@ -1,6 +1,6 @@
 """GPU parity of the dense TN, NN and TT layouts (fp8_gemm_tn: D = A^T B, A [K, M], B [K, N];
 fp8_gemm_nn: A [M, K], B [K, N]; fp8_gemm_tt: A [K, M], B [N, K]) against the CPU oracle
-(oracle.gemm_tn / gemm_nn / gemm_tt): both tile instances, ragged M / N tails with padded
+(oracle.gemm_tn / gemm_nn / gemm_tt): every tile instance, ragged M / N tails with padded
 leading dimensions, exact integer cases bit for bit (the library's bar otherwise), a
 strided and 2-byte-aligned D, and the dominant dense shape on sampled rows."""
 import numpy as np
@@ -15,10 +15,20 @@ from parity_util import bits_of, compare, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["128x128", "256x256"])
+@pytest.fixture(params=["128x128", "128x128-2stage", "256x256"])
 def tile(request):
-    fg.set_num_cus(1 if request.param == "256x256" else 1 << 20)
-    yield request.param
+    """The three instances: 128x128 tiles with the 4-stage ring (a plan whose units all
+    fit one round), 128x128 with the 2-stage ring (more units than CUs) and 256x256."""
+    if request.param == "128x128":
+        fg.set_num_cus(1 << 20)
+        yield request.param
+    else:
+        fg.set_num_cus(1)
+        if request.param == "256x256":
+            yield request.param
+        else:
+            with fg.force_config(128, 128, 1):
+                yield request.param
     fg.set_num_cus(0)
 
 
@@ -134,7 +144,7 @@ def test_degenerate_shapes(cuda_device, layout):
     D = c["D"].clone()
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     st = getattr(fg.lib(), "fp8_gemm_" + layout)(P(A), A.stride(0), P(c["sa"]), c["sa"].stride(0), P(B), B.stride(0),
-                                                 P(c["sb"]), P(D), D.stride(0), 0, 16, 128,
+                                                 P(c["sb"]), P(D), D.stride(0), 0, 16, 128, None, 0,
                                                  ctypes.c_void_p(torch.cuda.current_stream(cuda_device).cuda_stream))
     torch.cuda.synchronize()
     assert st == 0 and torch.equal(D.view(torch.int16), c["D"].view(torch.int16))
@@ -181,3 +191,91 @@ def test_c_parity_and_in_place(cuda_device, tile, layout, kind):
     fn(A, c["sa"], B, c["sb"], C, C=C)                      # in place: C is D
     torch.cuda.synchronize()
     compare(kind, bits_of(C), ref, f"{layout} C in place {tile} {kind}")
+
+
+# ---- split-K of the layout calls: forced splits over ragged K ranges (K = 1280: ten K
+# blocks in splits of 4, 4, 2 or 2, 2, 2, 2, 2 ...), M with a partly live 64-row half
+# (the fragments past M are not published), the UE8M0 and C forms, and the planner's own
+# split on the few-row shapes at full size
+def _layout_call(layout, c, At, Bt):
+    A = c["A"] if layout == "nn" else At
+    B = c["B"] if layout == "tt" else Bt
+    return A, B, {"tn": fg.fp8_gemm_tn, "nn": fg.fp8_gemm_nn, "tt": fg.fp8_gemm_tt}[layout]
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+@pytest.mark.parametrize("split", [2, 3, 10])
+@pytest.mark.parametrize("kind", ["normal", "e1"])
+@pytest.mark.parametrize("M,N,K", [(65, 200, 1280), (300, 520, 1280)])
+@pytest.mark.parametrize("ring", ["4-stage", "2-stage"])
+def test_split_k_parity(cuda_device, layout, split, kind, M, N, K, ring):
+    """ring: with 8 CUs assumed the units outnumber the CUs and the 2-stage instance runs."""
+    from parity_util import forced_workspace_bytes
+    c, At, Bt = tn_case(M, N, K, 5000 + split + M, cuda_device, kind)
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    fg.set_num_cus(8 if ring == "2-stage" else 0)
+    try:
+        ws = torch.zeros(forced_workspace_bytes(fg.KIND_LAYOUT, M, N, K, 1, (128, 128, split)), dtype=torch.uint8,
+                         device=cuda_device)
+        for rep in range(2):   # the counters the first call leaves serve the second
+            D = c["D"].clone()
+            with fg.force_config(128, 128, split):
+                fn(A, c["sa"], B, c["sb"], D, workspace=ws)
+            torch.cuda.synchronize()
+            compare(kind, bits_of(D), ref, f"{layout} split {split} {ring} {kind} {M}x{N}x{K} call {rep}")
+    finally:
+        fg.set_num_cus(0)
+    assert int(ws[:16384].view(torch.int32).abs().sum()) == 0   # every arrival counter reset
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+def test_split_k_ue8m0_and_c(cuda_device, layout):
+    from parity_util import forced_workspace_bytes
+    M, N, K = 130, 260, 1536
+    ws = torch.zeros(forced_workspace_bytes(fg.KIND_LAYOUT, M, N, K, 1, (128, 128, 4)), dtype=torch.uint8,
+                     device=cuda_device)
+    c, At, Bt = tn_case(M, N, K, 5100, cuda_device, "pow2")
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    D = c["D"].clone()
+    with fg.force_config(128, 128, 4):
+        fn(A, c["sa"], B, c["sb"], D, ue8m0=True, workspace=ws)
+    torch.cuda.synchronize()
+    compare("normal", bits_of(D), ref, f"{layout} ue8m0 split 4")
+    c, At, Bt = tn_case(M, N, K, 5101, cuda_device, "normal")
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    C = (torch.randn(M, N, generator=synth.make_generator(5102, cuda_device), device=cuda_device) * 0.5).to(
+        torch.bfloat16)
+    ref, _ = oracle.gemm_nt_c(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(),
+                              c["sb"].cpu().numpy(), bits_of(C))
+    with fg.force_config(128, 128, 4):
+        fn(A, c["sa"], B, c["sb"], C, C=C, workspace=ws)      # in place: C is D
+    torch.cuda.synchronize()
+    compare("normal", bits_of(C), ref, f"{layout} C in place split 4")
+
+
+def test_split_k_workspace_too_small_is_an_error(cuda_device):
+    M, N, K = 64, 256, 1024
+    c, At, Bt = tn_case(M, N, K, 5200, cuda_device, "e1")
+    ws = torch.zeros(1024, dtype=torch.uint8, device=cuda_device)
+    with fg.force_config(128, 128, 4):
+        with pytest.raises(fg.Fp8GemmError, match="workspace"):
+            fg.fp8_gemm_tn(At, c["sa"], Bt, c["sb"], c["D"].clone(), workspace=ws)
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (128, 7168, 2048)])
+def test_planner_split_few_row_full_size(cuda_device, layout, M, N, K):
+    """The few-row shapes at full size with the planner's own split (auto plan, library
+    workspace), against the oracle on every output."""
+    cfg = fg.query_config(fg.KIND_LAYOUT, M, N, K)
+    assert cfg["split_k"] > 1
+    c, At, Bt = tn_case(M, N, K, 5300 + M + N, cuda_device, "normal")
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    ws = fg.make_workspace(fg.KIND_LAYOUT, M, N, K, device=cuda_device)
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    compare("normal", bits_of(D), ref, f"{layout} {M}x{N}x{K} auto split {cfg['split_k']}")
