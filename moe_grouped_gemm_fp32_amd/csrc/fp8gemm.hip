@@ -687,7 +687,11 @@ int k_grouped_tn(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   const int bm = big ? 256 : 128, bn = big ? 256 : 128;
   p.tiles_m = (int)ceil_div(M, bm);
   p.tiles_n = (int)ceil_div(N, bn);
-  const int64_t tiles = (int64_t)G * p.tiles_m * p.tiles_n;
+  // chunks of one XCD's CUs worth of tiles, dealt to the XCDs in turn (the kernel's tile
+  // mapping); the grid covers whole rounds of chunks
+  p.chunk = std::max(1, std::min(cus / fp8gemm::kNumXcd, 64));
+  const int64_t chunks = (int64_t)G * ceil_div((int64_t)p.tiles_m * p.tiles_n, p.chunk);
+  const int64_t tiles = ceil_div(chunks, fp8gemm::kNumXcd) * fp8gemm::kNumXcd * p.chunk;
   if (tiles > INT32_MAX) return FP8GEMM_ERR_SHAPE;
   if (big && e8)
     hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, true>), dim3((unsigned)tiles), dim3(512), 0,

@@ -57,6 +57,7 @@ struct KParams {
   int split_k, kb_per_split;
   float* ws;
   int32_t* counters;
+  int chunk;  // K-grouped: tiles per chunk (the CUs of one XCD), see the tile mapping
   int kb_start[kMaxKGroups + 1];  // group g covers K blocks [kb_start[g], kb_start[g+1])
 };
 
@@ -113,14 +114,33 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   const int wave = uni(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // tile of this workgroup: XCD-contiguous ranges of a group-major (K-grouped) or
-  // split-major (dense layouts) rasterised order
+  // tile of this workgroup. Dense layouts: XCD-contiguous ranges of a split-major
+  // rasterised order. K-grouped: the groups' K lengths differ, so giving each XCD a
+  // contiguous range of a group-major order would leave the XCDs with the short groups
+  // idle while the one with the longest finishes (workgroup b always runs on XCD b % 8).
+  // Instead each group's tiles (in raster order) form chunks of p.chunk consecutive
+  // tiles, one per CU of an XCD, and the chunks, group after group, are dealt to the
+  // XCDs in turn: the i-th workgroup of XCD x takes tile i % chunk of chunk
+  // (i / chunk) * 8 + x. Every XCD gets a like mix of groups; the tiles that run together
+  // on one XCD are neighbours of one group and share its A and B panels in L2. The grid
+  // covers whole rounds of chunks; workgroups past a group's last tile exit at once.
   const int per_group = p.tiles_m * p.tiles_n;
   const int S = DENSE_TN ? p.split_k : 1;
-  const int L = xcd_remap(blockIdx.x, p.G * per_group * S);
-  const int g = DENSE_TN ? 0 : L / per_group;
-  const int split = DENSE_TN ? L / per_group : 0;
-  const int tile = L - (g + split) * per_group;
+  int g, split, tile;
+  if constexpr (DENSE_TN) {
+    const int L = xcd_remap(blockIdx.x, per_group * S);
+    g = 0;
+    split = L / per_group;
+    tile = L - split * per_group;
+  } else {
+    const int cpg = (per_group + p.chunk - 1) / p.chunk;  // chunks per group
+    const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+    const int k = (i / p.chunk) * kNumXcd + x;
+    g = k / cpg;
+    split = 0;
+    tile = (k - g * cpg) * p.chunk + i % p.chunk;
+    if (g >= p.G || tile >= per_group) return;  // the whole workgroup: no barrier is pending
+  }
   int tm, tn;
   raster(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
