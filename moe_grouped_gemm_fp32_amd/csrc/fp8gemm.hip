@@ -831,7 +831,8 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   if (M == 0) return FP8GEMM_OK;
   const size_t ws_avail = workspace ? workspace_bytes : 0;
   const LayoutPlan pl = choose_layout(M, N, K, cus, ws_avail);
-  if (pl.split > 1 && pl.tiles > kMaxSplitTiles) return FP8GEMM_ERR_CONFIG;
+  // only the 128x128 tiles split K
+  if (pl.split > 1 && (pl.tiles > kMaxSplitTiles || pl.bm != 128)) return FP8GEMM_ERR_CONFIG;
   if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
   if (pl.units > INT32_MAX) return FP8GEMM_ERR_SHAPE;
   fp8gemm::KParams p{};

@@ -308,9 +308,12 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     // fragments of this wave whose rows start below M (the few-row shapes leave whole
     // fragments past M)
     const int live_t = max(0, min(4, (p.M - m0 - 64 * wm + 15) >> 4));
-    if (S > 1 && !reduce_splits(p.ws, p.counters, acc, tile, split, S, (wave * 4 * TNW) * 64 + lane, BM * BN, tid,
-                                &s_last, live_t))
-      return;
+    // (K is split only with 64x64 wave tiles: the reduce of a 64x128 one would spill)
+    if constexpr (TNW == 4) {
+      if (S > 1 && !reduce_splits(p.ws, p.counters, acc, tile, split, S, (wave * 4 * TNW) * 64 + lane, BM * BN, tid,
+                                  &s_last, live_t))
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int m = m0 + 64 * wm + 16 * t + li;

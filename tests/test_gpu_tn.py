@@ -255,6 +255,16 @@ def test_split_k_ue8m0_and_c(cuda_device, layout):
     compare("normal", bits_of(C), ref, f"{layout} C in place split 4")
 
 
+def test_split_k_of_256_tiles_is_rejected(cuda_device):
+    """K is split only with 128x128 tiles (a 256x256 tile's reduce would spill)."""
+    M, N, K = 64, 256, 1024
+    c, At, Bt = tn_case(M, N, K, 5250, cuda_device, "e1")
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=cuda_device)
+    with fg.force_config(256, 256, 2):
+        with pytest.raises(fg.Fp8GemmError, match="configuration"):
+            fg.fp8_gemm_tn(At, c["sa"], Bt, c["sb"], c["D"].clone(), workspace=ws)
+
+
 def test_split_k_workspace_too_small_is_an_error(cuda_device):
     M, N, K = 64, 256, 1024
     c, At, Bt = tn_case(M, N, K, 5200, cuda_device, "e1")
