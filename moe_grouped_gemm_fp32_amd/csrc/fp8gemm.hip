@@ -40,6 +40,7 @@ std::mutex g_dev_mutex;
 std::atomic<int> g_num_cus_override{0};
 bool g_forced = false;
 fp8gemm_config_t g_forced_cfg{};
+std::atomic<uint32_t> g_forced_epoch{0};  // advanced by every fp8_gemm_force_config call
 
 int query_device(int* cus_out) {
   int dev = 0;
@@ -199,7 +200,7 @@ int64_t masked_capacity_tiles(int G, int M_max, int N, int expected_m, int bm, i
 
 // Choose tile shape and split for a call. `rows` is M (dense), M_total
 // (contiguous) or M_max (masked, where expected_m estimates the live rows).
-Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
+Plan choose_uncached(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
   Plan pl;
   const int num_kb = K / fp8gemm::kBlockK;
   if (g_forced) {
@@ -290,6 +291,31 @@ Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, si
   if ((pl.units > cap || kind == FP8GEMM_KIND_MASKED) && grid > fp8gemm::kNumXcd)
     grid = grid / fp8gemm::kNumXcd * fp8gemm::kNumXcd;
   pl.grid = (int)std::max<int64_t>(grid, 1);
+  return pl;
+}
+
+// The plan of a call depends only on its arguments below, so repeated calls of one shape
+// (a serving loop) take it from a small per-thread cache instead of re-running the
+// planner, which costs about a microsecond of host time per call.
+Plan choose(int kind, int rows, int N, int K, int G, int expected_m, int cus, size_t ws_avail) {
+  struct Entry {
+    int kind, rows, N, K, G, expected_m, cus;
+    uint32_t epoch;
+    size_t ws_avail;
+    bool valid;
+    Plan plan;
+  };
+  constexpr int kEntries = 16;
+  thread_local Entry cache[kEntries] = {};
+  const uint32_t epoch = g_forced_epoch.load(std::memory_order_acquire);
+  const uint64_t h = ((uint64_t)(uint32_t)rows * 0x9E3779B1u) ^ ((uint64_t)(uint32_t)N * 0x85EBCA77u) ^
+                     ((uint64_t)(uint32_t)K * 0xC2B2AE3Du) ^ (uint64_t)(kind * 31 + G);
+  Entry& e = cache[(h ^ (h >> 17)) % kEntries];
+  if (e.valid && e.kind == kind && e.rows == rows && e.N == N && e.K == K && e.G == G &&
+      e.expected_m == expected_m && e.cus == cus && e.epoch == epoch && e.ws_avail == ws_avail)
+    return e.plan;
+  const Plan pl = choose_uncached(kind, rows, N, K, G, expected_m, cus, ws_avail);
+  e = Entry{kind, rows, N, K, G, expected_m, cus, epoch, ws_avail, true, pl};
   return pl;
 }
 
@@ -1020,12 +1046,14 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m, 
 int fp8_gemm_force_config(const fp8gemm_config_t* cfg) {
   if (!cfg) {
     g_forced = false;
+    g_forced_epoch.fetch_add(1, std::memory_order_acq_rel);  // cached plans are stale
     return FP8GEMM_OK;
   }
   if (!(has_kernel(cfg->block_m, cfg->block_n) || is_layout_tile(cfg->block_m, cfg->block_n)) || cfg->split_k < 1)
     return FP8GEMM_ERR_CONFIG;
   g_forced_cfg = *cfg;
   g_forced = true;
+  g_forced_epoch.fetch_add(1, std::memory_order_acq_rel);
   return FP8GEMM_OK;
 }
 

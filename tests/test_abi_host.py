@@ -368,3 +368,34 @@ def test_packed_and_transform_argument_validation_without_launch():
     import torch
     if not torch.cuda.is_available():
         assert tr() == -5 and tr(act=0, ld_out=3) == -5
+
+
+def test_plan_cache_follows_forced_configs_and_arguments():
+    """The planner's per-thread cache returns the plan of the current arguments: forcing a
+    configuration, releasing it, another CU count or workspace size each give the plan the
+    planner computes for them."""
+    fg.set_num_cus(256)
+    try:
+        M, N, K = 64, 2112, 7168
+        auto = fg.query_config(fg.KIND_DENSE, M, N, K)
+        assert fg.query_config(fg.KIND_DENSE, M, N, K) == auto
+        with fg.force_config(128, 128, 3):
+            f = fg.query_config(fg.KIND_DENSE, M, N, K)
+            assert (f["block_m"], f["block_n"], f["split_k"]) == (128, 128, 3)
+        with fg.force_config(64, 128, 2):
+            f = fg.query_config(fg.KIND_DENSE, M, N, K)
+            assert (f["block_m"], f["block_n"], f["split_k"]) == (64, 128, 2)
+        assert fg.query_config(fg.KIND_DENSE, M, N, K) == auto
+        assert fg.query_config(fg.KIND_DENSE, M, N, K, workspace_bytes=0)["split_k"] == 1
+        fg.set_num_cus(64)
+        assert fg.query_config(fg.KIND_DENSE, M, N, K)["grid"] <= 64
+        fg.set_num_cus(256)
+        assert fg.query_config(fg.KIND_DENSE, M, N, K) == auto
+        # many shapes in turn (more than the cache holds) keep their own plans
+        shapes = [(m, n, k) for m in (64, 128, 4096) for n, k in ((2112, 7168), (24576, 1536), (7168, 2048))]
+        first = [fg.query_config(fg.KIND_DENSE, *sh) for sh in shapes]
+        for _ in range(3):
+            assert [fg.query_config(fg.KIND_DENSE, *sh) for sh in shapes] == first
+    finally:
+        fg.set_num_cus(0)
+
