@@ -458,11 +458,12 @@ int fp8_quantize_1x128(const void* X, int64_t ldx, int x_dtype, void* Q, int64_t
  * pages list runs linear 1, then SwiGLU, then linear 2 (es.news.hada.io/topic?id=19459,
  * "Mega MoE"), and the grouped calls compute the two linears. The SwiGLU reading (gate
  * half first, silu(x) = x * sigmoid(x)) is the standard one; the pages give no formula.
- * Per row r and column k < F, in FP32:
+ * Per row r and column k < F:
  *     y = silu(g) * u,  silu(g) = g / (1 + exp(-g)),  g = H[r][k], u = H[r][F + k]
- * then y is quantised exactly as by fp8_quantize_1x128 (s = amax / 448 per 128-column
- * block, q = e4m3_rne(y / s)). exp is the device's FP32 exponential (within a few
- * units in the last place), the division correctly rounded.
+ * evaluated in FP64 and rounded once to FP32 (the FP32 value nearest the exact y, but
+ * when that lies within ~2^-28 of an FP32 ulp of a rounding midpoint), then quantised
+ * exactly as by fp8_quantize_1x128 (s = amax / 448 per 128-column block, q =
+ * e4m3_rne(y / s)).
  *   H  [M, 2F] row-major (gate in columns 0..F-1, up in F..2F-1), row stride ldh
  *      (elements) >= 2F, BF16 or FP32 (h_dtype); 16-byte aligned, ldh a multiple
  *      of 8 (BF16) or 4 (FP32); F a positive multiple of 128.
