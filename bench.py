@@ -162,20 +162,28 @@ def kg_pmc_summary(args):
     print(json.dumps(out))
 
 
-def trace_summary(d, shapes, steps, warmup):
-    """Per-case GEMM kernel durations from a rocprofv3 --kernel-trace csv directory of a
-    default run with the same --steps / --warmup: the mean over all of a case's dispatches
-    and over the event-timed ones (the last `steps`), which the run's own HIP-event
-    figures cover."""
+def read_trace(d, kernel):
+    """(dispatch id, kernel name, duration ns) of every dispatch whose name contains
+    `kernel` in a rocprofv3 --kernel-trace csv directory, in dispatch order."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     rows = []
     for f in files:
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if "fp8_gemm_kernel" in r["Kernel_Name"]:
+                if kernel in r["Kernel_Name"]:
                     rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     rows.sort()
+    return rows
+
+
+def trace_summary(d, shapes, steps, warmup, kernel="fp8_gemm_kernel"):
+    """Per-case GEMM kernel durations from a rocprofv3 --kernel-trace csv directory of a
+    run with the same --steps / --warmup (the default run, or a dense-only one such as
+    --workload ue8m0 or --layout tn with kernel="fp8_k_grouped_tn_kernel"): the mean over
+    all of a case's dispatches and over the event-timed ones (the last `steps`), which the
+    run's own HIP-event figures cover."""
+    rows = read_trace(d, kernel)
     dense, small, grouped = dispatch_blocks(len(rows), shapes, steps, warmup)
 
     def stats(idx):
@@ -207,50 +215,64 @@ GROUPED_CASES = (["contiguous G=4 x 8192 rows N=4096 K=7168", "contiguous G=8 x 
                  ["moe gate+up N=4096 K=7168", "moe down N=7168 K=2048"])
 
 
-def trace_summary_grouped(d):
-    """Per-case average GEMM kernel duration of a --workload grouped run from a rocprofv3
+def trace_summary_cases(rows, names, steps):
+    """Per-case mean kernel duration over all dispatches and over the event-timed ones (the
+    last `steps` of each case) when dispatch i belongs to case i mod len(names)."""
+    for i, name in enumerate(names):
+        sel = rows[i::len(names)]
+        timed = sel[-steps:]
+        print(json.dumps({"case": name, "kernel": sel[0][1].replace("void fp8gemm::", ""),
+                          "dispatches": len(sel), "avg_us": round(sum(r[2] for r in sel) / len(sel) / 1e3, 2),
+                          "timed_avg_us": round(sum(r[2] for r in timed) / len(timed) / 1e3, 2)}))
+
+
+def trace_summary_grouped(d, steps):
+    """Per-case GEMM kernel durations of a --workload grouped run from a rocprofv3
     --kernel-trace csv directory. The first GEMM dispatch is the untimed gate+up call that
     produces the down GEMM's input; after it, dispatch i belongs to case i mod 14."""
-    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
-    rows = []
-    for f in files:
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                if "fp8_gemm_kernel" in r["Kernel_Name"]:
-                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
-                                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    rows.sort()
-    rows = rows[1:]
-    for i, name in enumerate(GROUPED_CASES):
-        sel = rows[i::len(GROUPED_CASES)]
-        us = sum(r[2] for r in sel) / len(sel) / 1e3
-        print(json.dumps({"case": name, "kernel": sel[0][1].replace("void fp8gemm::", ""),
-                          "dispatches": len(sel), "avg_us": round(us, 2)}))
+    trace_summary_cases(read_trace(d, "fp8_gemm_kernel")[1:], GROUPED_CASES, steps)
 
 
-def counter_summary(d, shapes, steps, warmup):
-    """Per-shape mean of every counter in a rocprofv3 --pmc csv directory of a default run
-    with the same --steps / --warmup (dense shapes only); values are summed over the
-    counter's hardware instances within a dispatch."""
+def read_counters(d, kernel):
+    """({(dispatch id, counter): value summed over the counter's hardware instances},
+    sorted dispatch ids, sorted counter names) of the dispatches whose kernel name
+    contains `kernel` in a rocprofv3 --pmc csv directory."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     per = {}
     for f in files:
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if "fp8_gemm_kernel" not in r["Kernel_Name"]:
+                if kernel not in r["Kernel_Name"]:
                     continue
                 key = (int(r["Dispatch_Id"]), r["Counter_Name"])
                 per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    dispatches = sorted({k[0] for k in per})
-    names = sorted({k[1] for k in per})
+    return per, sorted({k[0] for k in per}), sorted({k[1] for k in per})
+
+
+def counter_row(per, names, sel, row):
+    for c in names:
+        vals = [per[(x, c)] for x in sel if (x, c) in per]
+        row[c] = sum(vals) / len(vals) if vals else None
+    return row
+
+
+def counter_summary(d, shapes, steps, warmup, kernel="fp8_gemm_kernel"):
+    """Per-shape mean of every counter in a rocprofv3 --pmc csv directory of a run with
+    the same --steps / --warmup (the default run's dense shapes, or a dense-only run);
+    values are summed over the counter's hardware instances within a dispatch."""
+    per, dispatches, names = read_counters(d, kernel)
     dense, _, _ = dispatch_blocks(len(dispatches), shapes, steps, warmup)
     for i, (M, N, K) in enumerate(shapes):
         sel = [dispatches[j] for j in dense[i]]
-        row = {"M": M, "N": N, "K": K, "dispatches": len(sel)}
-        for c in names:
-            vals = [per[(x, c)] for x in sel if (x, c) in per]
-            row[c] = sum(vals) / len(vals) if vals else None
-        print(json.dumps(row))
+        print(json.dumps(counter_row(per, names, sel, {"M": M, "N": N, "K": K, "dispatches": len(sel)})))
+
+
+def counter_summary_cases(d, kernel, cases):
+    """Per-case counter means when dispatch i belongs to case i mod len(cases)."""
+    per, dispatches, names = read_counters(d, kernel)
+    for i, name in enumerate(cases):
+        sel = dispatches[i::len(cases)]
+        print(json.dumps(counter_row(per, names, sel, {"case": name, "dispatches": len(sel)})))
 
 
 def copy_only(args):
@@ -852,15 +874,24 @@ def main():
         kg_pmc_summary(args)
         return
     if args.counter_summary:
-        counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
-                        args.steps, args.warmup)
+        if args.workload == "kgrouped":
+            counter_summary_cases(args.counter_summary, "k_grouped_tn_kernel",
+                                  ["wgrad %dx%d" % mn for mn in KGROUP_CASES])
+        else:
+            counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
+                            args.steps, args.warmup,
+                            "fp8_gemm_kernel" if args.layout == "nt" else "fp8_k_grouped_tn_kernel")
         return
     if args.trace_summary:
         if args.workload == "grouped":
-            trace_summary_grouped(args.trace_summary)
+            trace_summary_grouped(args.trace_summary, args.steps)
+        elif args.workload == "kgrouped":
+            trace_summary_cases(read_trace(args.trace_summary, "k_grouped_tn_kernel"),
+                                ["wgrad %dx%d" % mn for mn in KGROUP_CASES], args.steps)
         else:
             trace_summary(args.trace_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
-                          args.steps, args.warmup)
+                          args.steps, args.warmup,
+                          "fp8_gemm_kernel" if args.layout == "nt" else "fp8_k_grouped_tn_kernel")
         return
     if args.copy_mb:
         copy_only(args)

@@ -67,9 +67,10 @@ def test_trace_summaries(tmp_path, capsys):
         for i in range(n):
             rows.append([2 + rep * n + i, "void fp8gemm::fp8_gemm_kernel<128, 128, 2, 2, 4, true>(fp8gemm::Params)", 0, 1000 * (i + 1)])
     _write_csv(str(tmp_path / "g" / "run_kernel_trace.csv"), ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
-    bench.trace_summary_grouped(str(tmp_path / "g"))
+    bench.trace_summary_grouped(str(tmp_path / "g"), steps=1)
     out = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
     assert len(out) == n and [o["avg_us"] for o in out] == [float(i + 1) for i in range(n)]
+    assert [o["timed_avg_us"] for o in out] == [float(i + 1) for i in range(n)]
 
 
 def test_default_run_dispatch_layout(tmp_path, capsys):
