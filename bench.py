@@ -267,9 +267,11 @@ def counter_summary(d, shapes, steps, warmup, kernel="fp8_gemm_kernel"):
         print(json.dumps(counter_row(per, names, sel, {"M": M, "N": N, "K": K, "dispatches": len(sel)})))
 
 
-def counter_summary_cases(d, kernel, cases):
-    """Per-case counter means when dispatch i belongs to case i mod len(cases)."""
+def counter_summary_cases(d, kernel, cases, skip=0):
+    """Per-case counter means when, after the first `skip` dispatches, dispatch i belongs
+    to case i mod len(cases)."""
     per, dispatches, names = read_counters(d, kernel)
+    dispatches = dispatches[skip:]
     for i, name in enumerate(cases):
         sel = dispatches[i::len(cases)]
         print(json.dumps(counter_row(per, names, sel, {"case": name, "dispatches": len(sel)})))
@@ -877,6 +879,8 @@ def main():
         if args.workload == "kgrouped":
             counter_summary_cases(args.counter_summary, "k_grouped_tn_kernel",
                                   ["wgrad %dx%d" % mn for mn in KGROUP_CASES])
+        elif args.workload == "grouped":   # the first dispatch is the untimed gate+up call
+            counter_summary_cases(args.counter_summary, "fp8_gemm_kernel", GROUPED_CASES, skip=1)
         else:
             counter_summary(args.counter_summary, parse_shapes(args.shapes) if args.shapes else CONFIG2,
                             args.steps, args.warmup,
