@@ -31,7 +31,10 @@ __all__ = [
     "Fp8GemmError",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8gemm.so")
+# FP8GEMM_LIBRARY names another build of the same library (the host-sanitizer build of
+# build.py); by default the one built in this directory
+LIB_PATH = os.environ.get("FP8GEMM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "libfp8gemm.so")
 KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_LAYOUT = 0, 1, 2, 3
 
 

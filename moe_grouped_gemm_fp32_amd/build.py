@@ -33,19 +33,60 @@ def command(out: str, extra=()) -> list:
             "-I", os.path.join(ROOT, "include"), *extra, SRC, "-o", out]
 
 
-def build(verbose: bool = True) -> str:
-    """Compile libfp8gemm.so next to this file (always rebuilds). Returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
+def _compile(cmd, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [tmp if c == out else c for c in cmd]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfp8gemm.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    """Compile libfp8gemm.so next to this file (always rebuilds). Returns its path."""
+    return _compile(command(LIB), LIB, verbose)
+
+
+# Host-sanitizer build: the same library with its host code (argument checks, planner,
+# plan cache, workspace and scratch bookkeeping) instrumented by AddressSanitizer and
+# UndefinedBehaviorSanitizer, every finding fatal. The device code is built as usual
+# (GPU sanitizers are not used). Load it with the sanitizer runtime preloaded
+# (sanitizer_runtime()) and FP8GEMM_LIBRARY pointing at it; it is for host-only checks.
+LIB_HOSTSAN = os.path.join(PKG, "libfp8gemm_hostsan.so")
+HOSTSAN_FLAGS = ["-Xarch_host", "-g", "-Xarch_host", "-fsanitize=address,undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of hipcc's clang (for LD_PRELOAD)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or clang
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc's clang was not found")
+    return path
+
+
+def build_host_sanitized(verbose: bool = True, force: bool = False) -> str:
+    """Compile libfp8gemm_hostsan.so next to this file unless it is newer than every
+    source. Returns its path."""
+    srcs = [SRC, *HEADERS, os.path.join(PKG, "csrc", "fp8kgroup_kernel.hpp"),
+            os.path.join(PKG, "csrc", "fp8quant_kernel.hpp"), os.path.abspath(__file__)]
+    if not force and os.path.exists(LIB_HOSTSAN) and \
+            os.path.getmtime(LIB_HOSTSAN) > max(os.path.getmtime(s) for s in srcs):
+        return LIB_HOSTSAN
+    return _compile(command(LIB_HOSTSAN, extra=HOSTSAN_FLAGS), LIB_HOSTSAN, verbose)
 
 
 if __name__ == "__main__":
-    build()
+    if "--host-sanitizers" in sys.argv[1:]:
+        build_host_sanitized(force=True)
+    else:
+        build()
