@@ -465,17 +465,16 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
-    // ---- contiguous: expert of this row block (-1 everywhere = nothing to do)
+    // ---- contiguous: expert of this row block, the largest m_indices entry of its rows
+    // (-1 everywhere = padding only: nothing to do). Each wave reduces it on its own, with
+    // cross-lane shuffles: no LDS and no workgroup barrier.
     if (p.kind == kContiguous) {
-      if (tid == 0) s_info = -1;
-      __syncthreads();
-      if (tid < BM && m0 + tid < p.M) {
-        const int e = p.m_indices[m0 + tid];
-        if (e >= 0) atomicMax(&s_info, e);
-      }
-      __syncthreads();
-      g = uni(s_info);
-      __syncthreads();
+      int e = -1;
+      for (int r = lane; r < BM; r += 64)
+        if (m0 + r < p.M) e = max(e, p.m_indices[m0 + r]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) e = max(e, __shfl_xor(e, off, 64));
+      g = uni(e);
       if (g < 0 || g >= p.G) continue;  // all padding (or an invalid id): nothing to write
     }
 
