@@ -418,7 +418,13 @@ int run(int kind, const char* name, Params& p, int rows, int N, int K, int G, in
   p.sb_kstride = p.sf_packed ? (p.num_kb + 3) / 4 : p.num_kb;
   p.num_units = (int)pl.units;
   p.full_tiles = (int)pl.full;
-  p.group_m = 8;
+  // Raster width (M tiles walked at a time). Dense calls with at most 16 K blocks walk
+  // one M-tile row at a time: their time goes largely into writing D, and the tiles that
+  // run together then cover whole output rows (measured: 4096x32768x512 8% faster,
+  // 4096x24576x1536 and 4096x7168x2048 3-5%). Longer K and the contiguous form keep 8,
+  // the better width for their operand reuse in L2 (with one row: 4096x4096x7168 3%
+  // slower, contiguous 8x4096 rows with K=2048 16% slower).
+  p.group_m = kind == FP8GEMM_KIND_DENSE && p.num_kb <= 16 ? 1 : 8;
   p.vec_store = (p.ldd % 8 == 0 && aligned(p.D, 16)) ? 2 : (p.ldd % 4 == 0 && aligned(p.D, 8)) ? 1 : 0;
   p.c_vec = p.C && p.ldc % 8 == 0 && aligned(p.C, 16) ? 1 : 0;
   if (pl.split > 1) {
