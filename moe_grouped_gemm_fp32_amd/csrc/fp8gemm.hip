@@ -777,8 +777,11 @@ bool is_layout_tile(int bm, int bn) { return (bm == 128 && bn == 128) || (bm == 
 // workspace holds the partials, choosing the split by a cost model fitted to measured
 // timings of every split of the few-row shapes (bench.py --plan-sweep layout): a unit
 // takes kLayoutKbUs per K block and the last arrival kLayoutSplitUs per further split
-// (publishing, arrival and reading a partial).
+// (publishing, arrival and reading a partial). A split unit keeps at least
+// kLayoutMinKbps K blocks: with fewer, its fixed cost (pipeline fill, partial) is not
+// amortised (measured: N=7168, K=2048 with 4 K blocks per unit 5-7% slower than with 6).
 constexpr int kLayoutMaxSplit = 16;
+constexpr int kLayoutMinKbps = 5;
 constexpr double kLayoutKbUs = 0.9;
 constexpr double kLayoutSplitUs = 1.0;
 LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
@@ -796,7 +799,7 @@ LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
     for (int sp = 1; sp <= std::min(num_kb, kLayoutMaxSplit); ++sp) {
       const int kbps = (int)ceil_div(num_kb, sp);
       if (ceil_div(num_kb, kbps) != sp) continue;  // the same as a smaller split
-      if (sp > 1 && (tiles * sp > cus || tiles > kMaxSplitTiles || split_ws_bytes(tiles, sp, 128, 128) > ws_avail))
+      if (sp > 1 && (kbps < kLayoutMinKbps || tiles * sp > cus || tiles > kMaxSplitTiles || split_ws_bytes(tiles, sp, 128, 128) > ws_avail))
         continue;
       const double t = kbps * kLayoutKbUs + (sp - 1) * kLayoutSplitUs;
       if (t < best) {
