@@ -521,7 +521,7 @@ def plan_sweep(args):
     torch.cuda.synchronize()
     layout = args.plan_sweep == "layout"
     tiles = [(128, 128), (256, 256)] if layout else [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128),
-                                                      (128, 256)]
+                                                      (128, 256), (64, 96), (128, 96)]
     for ti, t in enumerate(cases):
         nkb = t["K"] // 128
         masked = t["kind"] == fg.KIND_MASKED

@@ -98,9 +98,10 @@ struct Plan {
 struct Variant {
   int bm, bn, waves_m, waves_n, stages;
 };
+// The 96-column tiles (4 waves stacked along M) make 256 tiles of N=24576.
 constexpr Variant kVariants[] = {
     {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},  {128, 128, 2, 2, 4},
-    {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}};
+    {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}, {64, 96, 4, 1, 7},   {128, 96, 4, 1, 5}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kOccupancy = 1;
 
@@ -163,15 +164,18 @@ size_t split_ws_bytes(int64_t split_tiles, int split, int bm, int bn) {
 // The constants were fitted to measured timings of every tile / split / whole-tile-round
 // candidate of the 18 dense DeepSeek-V3-like shapes and the 10 masked decode cases, each
 // timed inside the benchmark's sequence of calls (two runs averaged; bench.py --plan-sweep,
-// the table in profiles/planner_sweep.json): with them the chosen plan is within 4.5% of
+// the table in profiles/planner_sweep.json): with them the chosen plan is within 2.5% of
 // the fastest measured one in all 28 cases.
 constexpr double kSplitUnitUs = 3.0;
 constexpr double kSplitReadUsPerKB = 0.03;
 // A call also takes at least its HBM traffic (A, B and D once, plus the split-K
-// partials, written and read once each) over an effective read rate of 3.5 TB/s, the
-// rate the few-row shapes (which stream B once) reach between back-to-back GEMMs. For
-// them this bound decides between tiles and splits that the per-unit costs rank wrongly.
+// partials, written and read once each) over an effective read rate, fitted like the
+// constants above: 4.2 TB/s for dense calls, whose few-row shapes stream B once at up to
+// 3.8-4.4 TB/s between back-to-back GEMMs, and 3.5 TB/s for the grouped calls. For the
+// few-row shapes this bound decides between tiles and splits that the per-unit costs
+// rank wrongly.
 constexpr double kHbmBytesPerUs = 3.5e6;
+constexpr double kDenseHbmBytesPerUs = 4.2e6;
 constexpr int kMaxSplit = 8;
 // Extra live M tiles per group the planner assumes for masked calls with several
 // groups: their live rows differ, so ceil(masked_m / BM) averages above expected_m / BM
@@ -187,6 +191,8 @@ UnitCost unit_cost(int bm, int bn) {
   if (bm == 128 && bn == 64) return {5.0, 0.60};
   if (bm == 64 && bn == 128) return {4.2, 0.59};
   if (bm == 256 && bn == 128) return {7.8, 0.85};
+  if (bm == 64 && bn == 96) return {5.0, 0.49};
+  if (bm == 128 && bn == 96) return {4.0, 0.56};
   return {8.3, 0.88};  // 128x256
 }
 
@@ -234,7 +240,8 @@ Plan choose_uncached(int kind, int rows, int N, int K, int G, int expected_m, in
       const double hbm_bytes = rows_live * K + (double)N * K * (kind == FP8GEMM_KIND_DENSE ? 1 : G) +
                                2.0 * rows_live * N +
                                8.0 * split * split_tiles * v.bm * v.bn;
-      const double t = std::max(t_units, hbm_bytes / kHbmBytesPerUs);
+      const double t =
+          std::max(t_units, hbm_bytes / (kind == FP8GEMM_KIND_DENSE ? kDenseHbmBytesPerUs : kHbmBytesPerUs));
       // ties of the bound (calls that stream the same bytes) go to the faster units
       if (t < best * 0.999 || (t < best * 1.001 && t_units < best_units)) {
         best = t;
@@ -247,6 +254,8 @@ Plan choose_uncached(int kind, int rows, int N, int K, int G, int expected_m, in
     };
     for (const auto& v : kVariants) {
       if (kind == FP8GEMM_KIND_CONTIGUOUS && 128 % v.bm != 0) continue;  // one expert per tile
+      // the 96-column tiles measure faster only on few-row dense calls (grouped calls: never)
+      if (kind != FP8GEMM_KIND_DENSE && v.bn % 128 != 0 && 128 % v.bn != 0) continue;
       if (v.bm >= 2 * 128 && live <= 128) continue;                      // mostly empty tiles
       // masked with several groups: their live rows differ, so the live M tiles per
       // group average more than expected_m / BM (by up to half a tile)

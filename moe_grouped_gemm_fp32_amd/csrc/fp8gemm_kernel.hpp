@@ -343,8 +343,16 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
   constexpr int TM = WTM / 16;
   constexpr int TN = WTN / 16;
   static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-  static_assert(kBlockK % WTN == 0, "a wave's columns must share one 128-column scale block");
   static_assert(TN % 2 == 0, "subtiles pair up into 16-byte stores");
+  // Weight scales per wave and K block: one when the wave's columns lie in one 128-column
+  // scale block (tile widths that are multiples or divisors of 128). Other widths (block
+  // sizes not aligned to the scale blocks, as on the DeepGEMM overview page,
+  // deepep.org/zh/deepgemm, 非对齐块大小: 96 columns make 256 tiles of N=24576) start
+  // tiles inside a scale block; there each 32-column pair of subtiles takes its own scale
+  // (32 divides both the tile width and 128, so a pair never straddles two blocks).
+  constexpr bool SB_ONE = (BN % kBlockK == 0 || kBlockK % BN == 0) && kBlockK % WTN == 0;
+  constexpr int NSB = SB_ONE ? 1 : TN / 2;
+  static_assert(SB_ONE || BN % 32 == 0, "unaligned tile widths are multiples of 32");
   static_assert((BM * kBlockK) % (1024 * NW) == 0 && (BN * kBlockK) % (1024 * NW) == 0, "tile load split");
   static_assert(STAGES >= 2, "pipeline depth");
   constexpr int A_BYTES = BM * kBlockK;
@@ -519,7 +527,10 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
       sc_src = sag + min(m0 + row, p.M - 1);
       sc_step = p.ld_sa;
     } else {
-      constexpr int NB = BN >= kBlockK ? BN / kBlockK : 1;
+      // the scale blocks the tile's columns touch: BN / 128, or, where a tile may start
+      // inside a block, one more than the blocks its width spans (slot nb holds block
+      // n0 / 128 + nb)
+      constexpr int NB = SB_ONE ? (BN >= kBlockK ? BN / kBlockK : 1) : (BN + kBlockK - 1) / kBlockK + 1;
       const int nb = min(lane, NB - 1);
       sc_src = sbg + (int64_t)(min(n0 + nb * kBlockK, p.N - 1) / kBlockK) * p.sb_kstride;
       sc_step = 1;
@@ -564,7 +575,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
     constexpr int NBUF = DB ? 2 : 1;
     constexpr int NREAD = TN + 1 + TM;
     v8i fa[NBUF][TM], fb[NBUF][TN];
-    float sa_r[NBUF][TM], sb_r[NBUF];  // raw scales; multiplied only once the stage is consumed
+    float sa_r[NBUF][TM], sb_r[NBUF][NSB];  // raw scales; multiplied only once the stage is consumed
     auto read_item = [&](int stage, auto buf_c, int q) {
       constexpr int buf = decltype(buf_c)::value;
       const uint8_t* sA = smem + stage * STAGE;
@@ -576,7 +587,12 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         const v4i hi = *reinterpret_cast<const v4i*>(sB + swz(row, fchunk + 1));
         fb[buf][q] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else if (q == TN) {
-        sb_r[buf] = sS[BM + (wn * WTN) / kBlockK];
+        if constexpr (SB_ONE) {
+          sb_r[buf][0] = sS[BM + (wn * WTN) / kBlockK];
+        } else {
+#pragma unroll
+          for (int h = 0; h < NSB; ++h) sb_r[buf][h] = sS[BM + ((n0 + wn * WTN + 32 * h) >> 7) - (n0 >> 7)];
+        }
         const float* sa_p = sS + wm * WTM + frow * TM;
         if constexpr (TM == 4) {
           const v4f v = *reinterpret_cast<const v4f*>(sa_p);
@@ -620,29 +636,34 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_gemm_kernel(con
         int ea[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t) ea[t] = (__float_as_int(sa_r[buf][t]) >> sh) & 0xFF;
-        const int eb = (__float_as_int(sb_r[buf]) >> sh) & 0xFF;
+        int eb[NSB];
+#pragma unroll
+        for (int h = 0; h < NSB; ++h) eb[h] = (__float_as_int(sb_r[buf][h]) >> sh) & 0xFF;
 #pragma unroll
         for (int k = 0; k < NMF; ++k) {
           const int t = k / TN, j = k % TN;
           acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[buf][j], fa[buf][t], acc[t][j], 0, 0,
-                                                                       0, eb, 0, ea[t]);
+                                                                       0, eb[SB_ONE ? 0 : j / 2], 0, ea[t]);
           side(k);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         return;
       }
-      float sc[TM];
+      float sc[TM][NSB];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) sc[t] = sa_r[buf][t] * sb_r[buf];
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int h = 0; h < NSB; ++h) sc[t][h] = sa_r[buf][t] * sb_r[buf][h];
       v4f r[NMF];
       auto promote = [&](int k) {
         const int t = k / TN, j = k % TN;
+        const float f = sc[t][SB_ONE ? 0 : j / 2];
         const v4f v = r[k];
-        acc[t][j][0] = __builtin_fmaf(v[0], sc[t], acc[t][j][0]);
-        acc[t][j][1] = __builtin_fmaf(v[1], sc[t], acc[t][j][1]);
-        acc[t][j][2] = __builtin_fmaf(v[2], sc[t], acc[t][j][2]);
-        acc[t][j][3] = __builtin_fmaf(v[3], sc[t], acc[t][j][3]);
+        acc[t][j][0] = __builtin_fmaf(v[0], f, acc[t][j][0]);
+        acc[t][j][1] = __builtin_fmaf(v[1], f, acc[t][j][1]);
+        acc[t][j][2] = __builtin_fmaf(v[2], f, acc[t][j][2]);
+        acc[t][j][3] = __builtin_fmaf(v[3], f, acc[t][j][3]);
       };
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {

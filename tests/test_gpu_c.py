@@ -13,7 +13,8 @@ from parity_util import SENT, bits_of, compare, forced_workspace_bytes, host, sa
 
 pytestmark = pytest.mark.gpu
 
-TILES = [None, (64, 64, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1), (64, 64, 3), (256, 128, 2), (128, 256, 2)]
+TILES = [None, (64, 64, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1), (64, 64, 3), (256, 128, 2), (128, 256, 2),
+         (64, 96, 1), (128, 96, 2)]
 
 
 def make_c(shape, kind, seed, device, scale=1.0):

@@ -13,8 +13,9 @@ from parity_util import SENT, assert_bit_exact, bits_of, compare, forced_workspa
 
 pytestmark = pytest.mark.gpu
 
-TILES = [(64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1),
-         (64, 64, 2), (128, 64, 3), (128, 128, 4), (256, 128, 2), (128, 256, 3)]
+TILES = [(64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1), (64, 96, 1),
+         (128, 96, 1), (64, 64, 2), (128, 64, 3), (128, 128, 4), (256, 128, 2), (128, 256, 3), (64, 96, 2),
+         (128, 96, 3)]
 CONFIG2_NK = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]
 COUNTER_BYTES = 16384  # the workspace's leading block of split-K arrival counters
 
@@ -54,7 +55,7 @@ def test_ragged_shapes_auto_and_forced(cuda_device, M, N, K, kind):
     ref, _ = oracle.gemm_nt(*host(c, "A", "sa", "B", "sb"))
     D, _ = run_dense(c)
     compare(kind, bits_of(D), ref, f"auto {M}x{N}x{K}")
-    for tile in [(64, 64, 1), (128, 128, 2), (64, 128, 3), (256, 128, 1), (128, 256, 2)]:
+    for tile in [(64, 64, 1), (128, 128, 2), (64, 128, 3), (256, 128, 1), (128, 256, 2), (64, 96, 1), (128, 96, 2)]:
         D, _ = run_dense(c, forced=tile)
         compare(kind, bits_of(D), ref, f"{tile} {M}x{N}x{K}")
 

@@ -47,7 +47,7 @@ def d_bits(c):
 
 @pytest.mark.parametrize("kind", ["normal", "e1", "e3"])
 @pytest.mark.parametrize("tile", [None, (64, 64, 1), (128, 128, 1), (64, 128, 1), (128, 64, 1), (64, 64, 2),
-                                  (128, 256, 1), (128, 256, 2)],
+                                  (128, 256, 1), (128, 256, 2), (64, 96, 1), (128, 96, 2)],
                          ids=lambda t: "auto" if t is None else "%dx%d_s%d" % t)
 def test_contiguous_small_all_tiles(cuda_device, kind, tile):
     c = synth.contiguous_case([5, 128, 0, 130, 1, 300], 200, 384, seed=41, device=cuda_device, kind=kind)
@@ -224,7 +224,8 @@ def test_masked_rejects_too_many_groups():
     assert st == -2
 
 
-@pytest.mark.parametrize("tile", [(64, 64, 2), (128, 128, 4), (256, 128, 3), (128, 256, 2), (64, 128, 8), (128, 64, 5)],
+@pytest.mark.parametrize("tile", [(64, 64, 2), (128, 128, 4), (256, 128, 3), (128, 256, 2), (64, 128, 8), (128, 64, 5),
+                                  (128, 96, 3)],
                          ids=lambda t: "%dx%d_s%d" % t)
 @pytest.mark.parametrize("kind", ["normal", "e1", "e1-ue8m0"])
 def test_masked_split_k_forced(cuda_device, tile, kind):

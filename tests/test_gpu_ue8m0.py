@@ -14,8 +14,8 @@ from parity_util import SENT, assert_bit_exact, bits_of, compare, forced_workspa
 
 pytestmark = pytest.mark.gpu
 
-TILES = [None, (64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1),
-         (64, 64, 3), (128, 128, 2), (256, 128, 2), (128, 256, 3)]
+TILES = [None, (64, 64, 1), (128, 64, 1), (64, 128, 1), (128, 128, 1), (256, 128, 1), (128, 256, 1), (64, 96, 1),
+         (64, 64, 3), (128, 128, 2), (256, 128, 2), (128, 256, 3), (128, 96, 2)]
 
 
 def run(c, tile=None):

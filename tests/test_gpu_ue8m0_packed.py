@@ -35,7 +35,7 @@ def run_dense(c, tile=None):
     return D, sa_w, sb_w
 
 
-TILES = [None, (64, 64, 1), (64, 64, 3), (128, 128, 2), (128, 64, 5), (256, 128, 1), (128, 256, 3)]
+TILES = [None, (64, 64, 1), (64, 64, 3), (128, 128, 2), (128, 64, 5), (256, 128, 1), (128, 256, 3), (64, 96, 2)]
 
 
 @pytest.mark.parametrize("kind", ["e1", "e3", "pow2"])
