@@ -25,8 +25,9 @@
 //   Promotion: the per-column scales make the factor sa[kb][m] * sb[kb][n] different for
 //   each element of a lane's four results (one m, four n), so it is formed per element:
 //   one multiply and one FMA per output element per K block, i.e. eight wave64 FP32
-//   operations (32 SIMD cycles) per 16x16x128 MFMA (also 32 cycles). That VALU work is as
-//   long as the matrix work and overlaps it only across the two waves of a SIMD.
+//   operations (32 SIMD cycles) per 16x16x128 MFMA (also 32 cycles), as long as the
+//   matrix work. The dense layouts' B scale covers a whole 128-column block, so there
+//   the factor is one product per row and the promotion four FMAs per MFMA.
 #pragma once
 
 #include "fp8gemm_kernel.hpp"
@@ -34,6 +35,7 @@
 namespace fp8gemm {
 
 constexpr int kMaxKGroups = 256;  // the K-block offsets travel in the kernel arguments
+constexpr int kDeferCols = 2;    // B columns of a block computed after the next block's barrier
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 
@@ -105,7 +107,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   constexpr int LPS = LPW + 1;                                   // + one scale load
   static_assert((LY::a_panels + LY::b_panels) * 16 == LPW * NW, "panel loads spread evenly");
   static_assert(BM + BN <= 64 * NW, "at most one scale load per wave");
-  static_assert(TNW % 4 == 0, "B fragments are read four at a time");
+  static_assert(TNW % 4 == 0, "the E8 form reads B fragments four at a time");
   static_assert(STAGES >= 2, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * LY::stage];
 
@@ -205,31 +207,62 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   // byte offset of logical chunk c (16 columns) of an operand tile
   auto frag_off = [&](int c) { return (c >> 3) * kPanel + rd_row * 128 + (((c & 7) ^ key) << 4) + 8 * (li & 1); };
   typedef __attribute__((address_space(3))) v2i_t* lds_v2i;
-  auto read_frag = [&](uint8_t* base) {
-    v2i_t x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(v2i_t*)(base + r * 8 * 128));
-    return v8i{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
-  };
+  // A fragment is read by RA (A) or RB (B) instructions: four transposing 8-byte reads
+  // of a K-major operand, or two 16-byte reads of a K-contiguous one. Read r fills
+  // elements [8 r / R, 8 (r + 1) / R) of the fragment.
+  constexpr int RA = A_KC ? 2 : 4, RB = B_KC ? 2 : 4;
   // K-contiguous operand: 16-row chunk c of the tile; lane 16 q + i takes row 16 c + i,
   // K bytes 32 q .. 32 q + 31 (logical 16-byte chunks 2q and 2q + 1)
-  auto read_frag_kc = [&](uint8_t* tile, int c) {
-    const int row = 16 * (c & 7) + li;
-    uint8_t* panel = tile + (c >> 3) * kPanel;
-    const uint4 lo = *reinterpret_cast<const uint4*>(panel + swz(row, 2 * q));
-    const uint4 hi = *reinterpret_cast<const uint4*>(panel + swz(row, 2 * q + 1));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  auto read_part = [&](uint8_t* tile, int c, int r, bool kc, v8i& f) {
+    if (kc) {
+      const int row = 16 * (c & 7) + li;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + (c >> 3) * kPanel + swz(row, 2 * q + r));
+      f[4 * r] = (int)v.x, f[4 * r + 1] = (int)v.y, f[4 * r + 2] = (int)v.z, f[4 * r + 3] = (int)v.w;
+    } else {
+      const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(v2i_t*)(tile + frag_off(c) + r * 8 * 128));
+      f[2 * r] = x[0], f[2 * r + 1] = x[1];
+    }
   };
-  auto frag_a = [&](uint8_t* st, int c) { return A_KC ? read_frag_kc(st, c) : read_frag(st + frag_off(c)); };
-  auto frag_b = [&](uint8_t* st, int c) {
-    return B_KC ? read_frag_kc(st + LY::b_off, c) : read_frag(st + LY::b_off + frag_off(c));
-  };
+  auto part_a = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st, c, r, A_KC, f); };
+  auto part_b = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st + LY::b_off, c, r, B_KC, f); };
 
   v4f acc[4][TNW];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int j = 0; j < TNW; ++j) acc[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // ---- K loop. Per block a wave issues 4 TNW MFMAs, B column chunk j (TNW wn + j)
+  // against its four A fragments t.
+  // FP32 scales: the B fragments stream. While the MFMAs of column j run, the wave reads
+  // column j + 1. The last ND columns of a block are deferred past the next block's
+  // barrier: their MFMAs then run while the new block's A fragments are read (each
+  // replacing an A fragment once the deferred MFMAs have consumed it). Each MFMA is one
+  // slot: the MFMA, its share of the reads, then the promotion of the MFMA two slots back,
+  // whose result is ready by then; scheduling barriers keep the slots in order. Before the
+  // first block the deferred columns are all zero operands with zero scales, so they add
+  // +0 exactly.
+  // E8 (no promotion): the wave reads its A fragments, then four B fragments at a time
+  // and issues their 16 MFMAs; left to the compiler's schedule this measured faster than
+  // the streamed order.
+  constexpr int ND = kDeferCols < TNW ? kDeferCols : TNW - 1;
+  constexpr int NMF = 4 * TNW, NDS = 4 * ND;  // slots per block, deferred slots
+  const int cb0 = TNW * wn;  // the wave's first 16-column chunk of the B tile
+  v8i fa[4], fb_last[ND];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fa[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int d = 0; d < ND; ++d) fb_last[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  // scales of the deferred columns: the per-row factors (the product with the B scale
+  // for the dense layouts, the A scale alone for the K-grouped form, whose B scales are
+  // per column, sb_last)
+  float s_last[4] = {0.f, 0.f, 0.f, 0.f};
+  v4f sb_last[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) sb_last[d] = v4f{0.f, 0.f, 0.f, 0.f};
+  // slot u: A fragment t and B column j (deferred: column TNW - ND + d of the last block)
+  auto slot_t = [](int u) { return u < NDS ? u / ND : (u - NDS) & 3; };
+  auto slot_j = [](int u) { return u < NDS ? TNW - ND + u % ND : (u - NDS) >> 2; };
 
   // STAGES-deep ring: blocks kb + 1 .. kb + STAGES - 2 stay in flight while block kb is
   // computed, and block kb + STAGES - 1 refills the slot of block kb - 1
@@ -239,6 +272,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   int slot = 0;
   for (int kb = 0; kb < nkb; ++kb) {
     wait_stages<LPS, STAGES - 2>(nkb - 1 - kb);  // this wave's loads of block kb have landed
+    wait_lgkmcnt0();   // and its reads of block kb - 1 (the deferred columns' B fragments)
     barrier();         // everyone's have, and everyone is done reading block kb - 1
     if (kb + STAGES - 1 < nkb) issue(kb + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
 
@@ -246,27 +280,29 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     slot = slot == STAGES - 1 ? 0 : slot + 1;
     const float* s_a = reinterpret_cast<const float*>(st + LY::s_off);
     const float* s_b = s_a + BM;
-    v8i fa[4];
     float sa_t[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      fa[t] = frag_a(st, 4 * wm + t);
-      sa_t[t] = s_a[64 * wm + 16 * t + li];
-    }
+    for (int t = 0; t < 4; ++t) sa_t[t] = s_a[64 * wm + 16 * t + li];
+
     if constexpr (E8) {
       // operand scales: lane l carries the exponent of its A row 16 t + l % 16 and of its
       // B row 16 j + l % 16 (the same for its four 32-K chunks: one block scale)
       int ea[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ea[t] = (__float_as_int(sa_t[t]) >> 23) & 0xFF;
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < RA; ++r) part_a(st, 4 * wm + t, r, fa[t]);
+        ea[t] = (__float_as_int(sa_t[t]) >> 23) & 0xFF;
+      }
 #pragma unroll
       for (int jh = 0; jh < TNW / 4; ++jh) {
         v8i fb[4];
         int eb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          fb[j] = frag_b(st, TNW * wn + 4 * jh + j);
-          eb[j] = (__float_as_int(s_b[16 * (TNW * wn + 4 * jh + j) + li]) >> 23) & 0xFF;
+#pragma unroll
+          for (int r = 0; r < RB; ++r) part_b(st, cb0 + 4 * jh + j, r, fb[j]);
+          eb[j] = (__float_as_int(s_b[16 * (cb0 + 4 * jh + j) + li]) >> 23) & 0xFF;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -277,28 +313,91 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
       }
       continue;
     }
+
+    // dense layouts: the wave's 16 TNW columns lie in one 128-column block of B, whose
+    // scale every column entry repeats
+    const float sbw = DENSE_TN ? s_b[16 * cb0] : 0.f;
+    v4f sbc[TNW];   // K-grouped form: B scales of the lane's four columns of chunk j
+    v8i fb[TNW];
 #pragma unroll
-    for (int jh = 0; jh < TNW / 4; ++jh) {
-      v8i fb[4];
-      v4f sb_j[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        fb[j] = frag_b(st, TNW * wn + 4 * jh + j);
-        sb_j[j] = *reinterpret_cast<const v4f*>(s_b + 16 * TNW * wn + 16 * (4 * jh + j) + 4 * q);
+    for (int r = 0; r < RB; ++r) part_b(st, cb0, r, fb[0]);
+    auto col_scale = [&](int j) {
+      if constexpr (!DENSE_TN) sbc[j] = *reinterpret_cast<const v4f*>(s_b + 16 * (cb0 + j) + 4 * q);
+    };
+    col_scale(0);
+
+    v4f res[NMF];
+    auto promote = [&](int u) {
+      const v4f v = res[u];
+      const bool def = u < NDS;
+      const int t = slot_t(u), j = slot_j(u);
+      v4f s;
+      if constexpr (DENSE_TN) {
+        const float f = def ? s_last[t] : sa_t[t] * sbw;
+        s = v4f{f, f, f, f};
+      } else {
+        s = def ? sb_last[u % ND] * s_last[t] : sbc[j] * sa_t[t];
       }
+      v4f& a = acc[t][j];
+      a[0] = __builtin_fmaf(v[0], s[0], a[0]);
+      a[1] = __builtin_fmaf(v[1], s[1], a[1]);
+      a[2] = __builtin_fmaf(v[2], s[2], a[2]);
+      a[3] = __builtin_fmaf(v[3], s[3], a[3]);
+    };
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+    for (int u = 0; u < NMF; ++u) {
+      const bool def = u < NDS;
+      const int t = slot_t(u), j = slot_j(u);
+      res[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(def ? fb_last[u % ND] : fb[j], fa[t],
+                                                                v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      if (def) {
+        // the last deferred MFMA of A fragment t has read it: read this block's
+        if (u % ND == ND - 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[t], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                          0, 0, 0, 0, 0, 0);
-          const v4f s = sb_j[j] * sa_t[t];
-          v4f& a = acc[t][4 * jh + j];
-          a[0] = __builtin_fmaf(r[0], s[0], a[0]);
-          a[1] = __builtin_fmaf(r[1], s[1], a[1]);
-          a[2] = __builtin_fmaf(r[2], s[2], a[2]);
-          a[3] = __builtin_fmaf(r[3], s[3], a[3]);
+          for (int r = 0; r < RA; ++r) part_a(st, 4 * wm + t, r, fa[t]);
         }
+      } else {
+        // column j reads column j + 1, the last regular column also the deferred ones;
+        // their parts go out in the first three slots (the first takes the extra), so the
+        // last lands two MFMAs before its first use
+        const int c1 = j + 1, c2 = j == TNW - ND - 1 ? TNW - 1 : j + 1;
+        const int nparts = (c2 - c1 + 1) * RB;
+#pragma unroll
+        for (int p = 0; p < nparts; ++p)
+          if (p * 3 / nparts == t) part_b(st, cb0 + c1 + p / RB, p % RB, fb[c1 + p / RB]);
+        if (t == 2)
+#pragma unroll
+          for (int c = c1; c <= c2; ++c) col_scale(c);
+      }
+      if (u >= 2) promote(u - 2);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    promote(NMF - 2);
+    promote(NMF - 1);
+    // the last ND columns wait for the next block (or the drain below)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      fb_last[d] = fb[TNW - ND + d];
+      if constexpr (!DENSE_TN) sb_last[d] = sbc[TNW - ND + d];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s_last[t] = DENSE_TN ? sa_t[t] * sbw : sa_t[t];
+  }
+  // drain: the deferred columns of the last block
+  if constexpr (!E8) {
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) {
+      const int t = slot_t(u), j = slot_j(u), d = u % ND;
+      const v4f v = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb_last[d], fa[t], v4f{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                     0, 0, 0, 0, 0);
+      const v4f s = DENSE_TN ? v4f{s_last[t], s_last[t], s_last[t], s_last[t]} : sb_last[d] * s_last[t];
+      v4f& a = acc[t][j];
+      a[0] = __builtin_fmaf(v[0], s[0], a[0]);
+      a[1] = __builtin_fmaf(v[1], s[1], a[1]);
+      a[2] = __builtin_fmaf(v[2], s[2], a[2]);
+      a[3] = __builtin_fmaf(v[3], s[3], a[3]);
     }
   }
 
