@@ -781,7 +781,10 @@ struct LayoutPlan {
 
 bool is_layout_tile(int bm, int bn) { return (bm == 128 && bn == 128) || (bm == 256 && bn == 256); }
 
-// 256x256 tiles once they alone give every CU a tile. Otherwise 128x128 tiles; when
+// 256x256 tiles once they give at least half the CUs a tile and pad the output by at most
+// a quarter: a CU computes a 256x256 tile ~20% faster than two co-resident 128x128 ones
+// (measured: 4096x2112x7168, 144 such tiles, 99 vs 120 us), but a few-row shape would
+// compute its padding. Otherwise 128x128 tiles; when
 // those leave CUs idle, K is split as far as all units still run in one round and the
 // workspace holds the partials, choosing the split by a cost model fitted to measured
 // timings of every split of the few-row shapes (bench.py --plan-sweep layout): a unit
@@ -800,7 +803,8 @@ LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
     pl.bm = g_forced_cfg.block_m;
     pl.bn = g_forced_cfg.block_n;
     pl.split = std::max(1, std::min(g_forced_cfg.split_k, num_kb));
-  } else if (ceil_div(M, 256) * ceil_div(N, 256) >= cus) {
+  } else if (2 * ceil_div(M, 256) * ceil_div(N, 256) >= cus &&
+             (double)(ceil_div(M, 256) * 256) * (double)(ceil_div(N, 256) * 256) <= 1.25 * (double)M * N) {
     pl.bm = pl.bn = 256;
   } else {
     const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);

@@ -257,17 +257,22 @@ def test_layout_argument_validation_without_launch(name, a_kc, b_kc):
 
 
 def test_layout_planner_splits_few_row_shapes():
-    """The TN / NN / TT plan: 256x256 tiles when they fill the CUs, 128x128 otherwise;
-    K split (at least two K blocks a unit) when the 128x128 tiles leave more than half the
-    CUs idle and the workspace holds the partials; no split without a workspace."""
+    """The TN / NN / TT plan: 256x256 tiles when they give at least half the CUs a tile and
+    pad the output by at most a quarter, 128x128 otherwise; K split (at least two K blocks
+    a unit) when the 128x128 tiles leave more than half the CUs idle and the workspace holds
+    the partials; no split without a workspace."""
     fg.set_num_cus(256)
     try:
         L = fg.KIND_LAYOUT
         big = fg.query_config(L, 4096, 7168, 16384)
         assert (big["block_m"], big["block_n"], big["split_k"]) == (256, 256, 1)
         assert fg.workspace_size(L, 4096, 7168, 16384) == 0
-        mid = fg.query_config(L, 4096, 2112, 7168)     # 544 tiles of 128x128
-        assert (mid["block_m"], mid["split_k"]) == (128, 1)
+        mid = fg.query_config(L, 4096, 2112, 7168)     # 144 tiles of 256x256, N padded by 9%
+        assert (mid["block_m"], mid["block_n"], mid["split_k"]) == (256, 256, 1)
+        small = fg.query_config(L, 2048, 2048, 7168)   # 64 tiles of 256x256: 256 of 128x128
+        assert (small["block_m"], small["split_k"]) == (128, 1)
+        wide = fg.query_config(L, 128, 32768, 512)     # 128 tiles of 256x256 would double the rows
+        assert (wide["block_m"], wide["split_k"]) == (128, 1)
         for M, N, K in [(64, 2112, 7168), (128, 7168, 2048), (128, 4096, 7168)]:
             cfg = fg.query_config(L, M, N, K)
             tiles = fg.num_tiles(M, N, 128, 128)
