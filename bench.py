@@ -520,7 +520,7 @@ def plan_sweep(args):
                                                                                 c["D"], c["masked_m"], 256, WS))))
     torch.cuda.synchronize()
     layout = args.plan_sweep == "layout"
-    tiles = [(128, 128), (256, 256)] if layout else [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128),
+    tiles = [(128, 128), (256, 256), (64, 128), (128, 64)] if layout else [(64, 64), (128, 64), (64, 128), (128, 128), (256, 128),
                                                       (128, 256), (64, 96), (128, 96)]
     for ti, t in enumerate(cases):
         nkb = t["K"] // 128

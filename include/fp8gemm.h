@@ -502,8 +502,8 @@ int fp8_gemm_query_config(int kind, int M, int N, int K, int G, int expected_m,
  * Returns FP8GEMM_ERR_CONFIG for a tile shape that no call has a kernel for; a later
  * call returns FP8GEMM_ERR_CONFIG if it has no kernel for the forced tile (the NT and
  * M-grouped calls: 64x64, 128x64, 64x128, 128x128, 256x128, 128x256, 64x96, 128x96; the TN / NN / TT
- * calls: 128x128, 256x256, which ignore full_tiles and split K only with 128x128) or if
- * the forced plan splits more than 4096 tiles. */
+ * calls: 128x128, 256x256, 64x128, 128x64, which ignore full_tiles and do not split K
+ * with 256x256) or if the forced plan splits more than 4096 tiles. */
 int fp8_gemm_force_config(const fp8gemm_config_t* cfg);
 
 /* Cap on the compute units the persistent grid is sized for: the analog of

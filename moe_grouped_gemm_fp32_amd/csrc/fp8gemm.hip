@@ -772,30 +772,35 @@ namespace {
 // Tile plans of the dense layout calls (TN, NN, TT). Instances: 256x256 tiles (8 waves of
 // 64x128, a 2-stage ring); 128x128 tiles (4 waves of 64x64) with a 2-stage ring, of
 // which two workgroups share a CU, or a 4-stage ring (one workgroup per CU, more bytes
-// in flight per unit) for plans whose units all run in one round.
+// in flight per unit) for plans whose units all run in one round; 64x128 and 128x64
+// tiles (4 waves of 64x32; one operand in a 64-wide panel) with a 6-stage ring.
 struct LayoutPlan {
   int bm = 128, bn = 128, split = 1, kbps = 0, stages = 2;
   int64_t tiles = 0, units = 0;
   size_t ws_bytes = 0;
 };
 
-bool is_layout_tile(int bm, int bn) { return (bm == 128 && bn == 128) || (bm == 256 && bn == 256); }
+bool is_layout_tile(int bm, int bn) {
+  return (bm == 128 && bn == 128) || (bm == 256 && bn == 256) || (bm == 64 && bn == 128) || (bm == 128 && bn == 64);
+}
 
 // 256x256 tiles once they give at least half the CUs a tile and pad the output by at most
 // a quarter: a CU computes a 256x256 tile ~20% faster than two co-resident 128x128 ones
 // (measured: 4096x2112x7168, 144 such tiles, 99 vs 120 us), but a few-row shape would
-// compute its padding. Otherwise 128x128 tiles; when
-// those leave CUs idle, K is split as far as all units still run in one round and the
-// workspace holds the partials, choosing the split by a cost model fitted to measured
-// timings of every split of the few-row shapes (bench.py --plan-sweep layout): a unit
-// takes kLayoutKbUs per K block and the last arrival kLayoutSplitUs per further split
-// (publishing, arrival and reading a partial). A split unit keeps at least
-// kLayoutMinKbps K blocks: with fewer, its fixed cost (pipeline fill, partial) is not
-// amortised (measured: N=7168, K=2048 with 4 K blocks per unit 5-7% slower than with 6).
+// compute its padding. Otherwise the tile (128x128, 64x128 or 128x64) and the K split
+// with the least modelled time. These calls are bound by what each CU streams: a unit
+// costs kLayoutUsPerLoadByte per byte of its K blocks' loads (the whole tile, rows past
+// M included) plus kLayoutUnitUs, per round of units, and the last arrival
+// kLayoutUsPerPartialByte per byte of each further partial it reads (live rows only).
+// Constants fitted to bench.py --plan-sweep layout (every tile and split of the 12 few-row
+// shapes; the choice is within 5% of the fastest measured plan on each). K is split only
+// as far as all units run in one round, each keeps at least kLayoutMinKbps K blocks (with
+// fewer, its fixed cost is not amortised) and the workspace holds the partials.
 constexpr int kLayoutMaxSplit = 16;
 constexpr int kLayoutMinKbps = 5;
-constexpr double kLayoutKbUs = 0.9;
-constexpr double kLayoutSplitUs = 1.0;
+constexpr double kLayoutUsPerLoadByte = 2.57e-5;
+constexpr double kLayoutUsPerPartialByte = 2.72e-5;
+constexpr double kLayoutUnitUs = 8.66;
 LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
   LayoutPlan pl;
   const int num_kb = K / fp8gemm::kBlockK;
@@ -807,17 +812,27 @@ LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
              (double)(ceil_div(M, 256) * 256) * (double)(ceil_div(N, 256) * 256) <= 1.25 * (double)M * N) {
     pl.bm = pl.bn = 256;
   } else {
-    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    static const int kTiles[3][2] = {{128, 128}, {64, 128}, {128, 64}};
     double best = 1e30;
-    for (int sp = 1; sp <= std::min(num_kb, kLayoutMaxSplit); ++sp) {
-      const int kbps = (int)ceil_div(num_kb, sp);
-      if (ceil_div(num_kb, kbps) != sp) continue;  // the same as a smaller split
-      if (sp > 1 && (kbps < kLayoutMinKbps || tiles * sp > cus || tiles > kMaxSplitTiles || split_ws_bytes(tiles, sp, 128, 128) > ws_avail))
-        continue;
-      const double t = kbps * kLayoutKbUs + (sp - 1) * kLayoutSplitUs;
-      if (t < best) {
-        best = t;
-        pl.split = sp;
+    for (const auto& tl : kTiles) {
+      const int bm = tl[0], bn = tl[1];
+      const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+      for (int sp = 1; sp <= std::min(num_kb, kLayoutMaxSplit); ++sp) {
+        const int kbps = (int)ceil_div(num_kb, sp);
+        if (ceil_div(num_kb, kbps) != sp) continue;  // the same as a smaller split
+        if (sp > 1 && (kbps < kLayoutMinKbps || tiles * sp > cus || tiles > kMaxSplitTiles ||
+                       split_ws_bytes(tiles, sp, bm, bn) > ws_avail))
+          continue;
+        const int64_t units = tiles * sp;
+        // two 2-stage 128x128 workgroups share a CU; the 6-stage narrow tiles take one
+        const int per_cu = (bm == 128 && bn == 128 && units > cus) ? 2 : 1;
+        const double rounds = (double)ceil_div(units, (int64_t)cus * per_cu);
+        const double t = rounds * ((double)kbps * (bm + bn) * fp8gemm::kBlockK * kLayoutUsPerLoadByte + kLayoutUnitUs) +
+                         (sp - 1) * (double)std::min(bm, M) * bn * 4 * kLayoutUsPerPartialByte;
+        if (t < best) {
+          best = t;
+          pl.bm = bm, pl.bn = bn, pl.split = sp;
+        }
       }
     }
   }
@@ -826,7 +841,7 @@ LayoutPlan choose_layout(int M, int N, int K, int cus, size_t ws_avail) {
   pl.tiles = ceil_div(M, pl.bm) * ceil_div(N, pl.bn);
   pl.units = pl.tiles * pl.split;
   pl.ws_bytes = split_ws_bytes(pl.tiles, pl.split, pl.bm, pl.bn);
-  pl.stages = (pl.bm == 128 && pl.units <= cus) ? 4 : 2;
+  pl.stages = pl.bm == 256 ? 2 : pl.bm == 64 || pl.bn == 64 ? 6 : pl.units <= cus ? 4 : 2;
   return pl;
 }
 
@@ -835,6 +850,12 @@ void launch_dense_layout(const fp8gemm::KParams& p, const LayoutPlan& pl, hipStr
   const dim3 grid((unsigned)pl.units);
   if (pl.bm == 256)
     hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<4, 2, 8, 2, E8, true, A_KC, B_KC>), grid, dim3(512), 0,
+                       stream, p);
+  else if (pl.bm == 64)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<1, 4, 2, 6, E8, true, A_KC, B_KC>), grid, dim3(256), 0,
+                       stream, p);
+  else if (pl.bn == 64)
+    hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 2, 6, E8, true, A_KC, B_KC>), grid, dim3(256), 0,
                        stream, p);
   else if (pl.stages == 4)
     hipLaunchKernelGGL((fp8gemm::fp8_k_grouped_tn_kernel<2, 2, 4, 4, E8, true, A_KC, B_KC>), grid, dim3(256), 0,
@@ -879,8 +900,8 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   if (M == 0) return FP8GEMM_OK;
   const size_t ws_avail = workspace ? workspace_bytes : 0;
   const LayoutPlan pl = choose_layout(M, N, K, cus, ws_avail);
-  // only the 128x128 tiles split K
-  if (pl.split > 1 && (pl.tiles > kMaxSplitTiles || pl.bm != 128)) return FP8GEMM_ERR_CONFIG;
+  // the 256x256 tiles do not split K
+  if (pl.split > 1 && (pl.tiles > kMaxSplitTiles || pl.bm == 256)) return FP8GEMM_ERR_CONFIG;
   if (pl.split > 1 && pl.ws_bytes > ws_avail) return FP8GEMM_ERR_WORKSPACE;
   if (pl.units > INT32_MAX) return FP8GEMM_ERR_SHAPE;
   fp8gemm::KParams p{};
@@ -899,6 +920,7 @@ int dense_layout(const void* A, int64_t lda, const float* sa, int64_t ld_sa, con
   p.vec4 = (ldd % 4 == 0 && aligned(D, 8)) ? 1 : 0;
   p.tiles_m = (int)ceil_div(M, pl.bm);
   p.tiles_n = (int)ceil_div(N, pl.bn);
+  p.stream_b = p.tiles_m == 1 ? 1 : 0;
   p.split_k = pl.split;
   p.kb_per_split = pl.kbps;
   if (pl.split > 1) {

@@ -11,11 +11,13 @@
 // [K/128][ld_sb]). D is FP32 [G][M][N]; C is the old D when accumulating, else +0.
 //
 // Data path per BM x BN output tile (one workgroup of WAVES_M x WAVES_N wave64s, each
-// computing 64 x 16 TNW outputs; instances 128x128 with 2x2 waves and 256x256 with 4x2):
-//   a STAGES-deep LDS ring (2 in both instances) holding, per 128-row K block, the A tile as BM/128 panels of
-//   [128 k][128 m] bytes, the B tile as BN/128 panels of [128 k][128 n], and the block's
-//   BM + BN scales, filled by direct-to-LDS loads (16 bytes per lane, 8 lanes per
-//   128-byte panel row; every wave issues 8 of them and one scale load per block). The
+// computing 64 x 16 TNW outputs; instances 128x128 with 2x2 waves, 256x256 with 4x2, and
+// for the dense layouts' few-row shapes 64x128 (1x4 waves) and 128x64 (2x2 waves of 64x32)):
+//   a STAGES-deep LDS ring holding, per 128-row K block, the A tile as [128 k][128 m] byte
+//   panels (one [128 k][64 m] panel when BM = 64), the B tile likewise, and the block's
+//   BM + BN scales, filled by direct-to-LDS loads (16 bytes per lane, 8 lanes per 128-byte
+//   panel row, 4 per 64-byte row; one kilobyte per load instruction, spread evenly over
+//   the waves, and one scale load per wave per block). The
 //   FP8 MFMA wants each lane's 32 operand bytes to be 32 K values of one row, so the
 //   fragments are read with gfx950's transposing LDS read ds_read_b64_tr_b8: within each
 //   16-lane group, output lane i gets byte (i & 7) of the 8-byte rows addressed by lanes
@@ -60,23 +62,38 @@ struct KParams {
   float* ws;
   int32_t* counters;
   int chunk;  // K-grouped: tiles per chunk (the CUs of one XCD), see the tile mapping
+  // dense layouts: 1 when one tile row covers all of M, so that each B tile is read by one
+  // unit: B is then loaded with the non-temporal hint (streamed past the caches, which
+  // keep A; measured on the few-row shapes: up to 22% faster, where B tiles are shared
+  // up to 18% slower)
+  int stream_b;
   int kb_start[kMaxKGroups + 1];  // group g covers K blocks [kb_start[g], kb_start[g+1])
 };
 
 namespace kg {
 constexpr int kPanel = 128 * 128;  // one [128 k][128 columns] byte panel of a K block
+// A stage holds the A tile (BM columns or rows by 128 K bytes), then B (BN by 128), then
+// the scales. A K-major operand of 128 or more columns is stored as [128 k][128 columns]
+// panels; one of 64 columns as a single [128 k][64 columns] panel (64-byte rows). A
+// K-contiguous operand is stored as [rows][128 k] (128-row panels, or one of 64 rows).
 template <int BM, int BN, int NW>
 struct Layout {
-  static constexpr int a_panels = BM / 128, b_panels = BN / 128;
-  static constexpr int b_off = a_panels * kPanel;
-  static constexpr int s_off = (a_panels + b_panels) * kPanel;  // sa[BM] then sb[BN]
-  static constexpr int stage = s_off + NW * 256;                // one 64-scale load per wave
+  static constexpr int wa = BM < 128 ? BM : 128, wb = BN < 128 ? BN : 128;  // panel widths
+  static constexpr int la = BM * kBlockK / 1024, lb = BN * kBlockK / 1024;  // 1 KB loads per block
+  static constexpr int b_off = BM * kBlockK;
+  static constexpr int s_off = (BM + BN) * kBlockK;  // sa[BM] then sb[BN]
+  static constexpr int stage = s_off + NW * 256;     // one 64-scale load per wave
 };
 
-// 16-byte chunk position of logical chunk c in K row k of a panel. With it, the 32 lanes
-// of each half-wave of a fragment read (16 K rows, both 8-byte halves of one chunk)
-// touch 32 distinct 8-byte bank slots.
+// 16-byte chunk position of logical chunk c in K row k of a panel: c ^ chunk_key(k) in a
+// 128-wide panel, c ^ chunk_key64(k) in a 64-wide one. With it, the 32 lanes of each
+// half-wave of a fragment read (16 K rows, both 8-byte halves of one chunk) touch 32
+// distinct 8-byte slots of a 256-byte bank row: in a 128-wide panel the rows alternate
+// between the two 128-byte halves and the key spreads the chunks; in a 64-wide panel
+// four rows share a bank row and the key gives those four (rows 4 and 32 apart) four
+// distinct chunk positions.
 __device__ __forceinline__ int chunk_key(int k) { return ((k >> 1) & 3) | ((k >> 3) & 4); }
+__device__ __forceinline__ int chunk_key64(int k) { return ((k >> 2) & 1) | ((k >> 4) & 2); }
 }  // namespace kg
 
 // E8 instances take power-of-two scales (UE8M0 values 2^(e-127) held as FP32): the
@@ -103,11 +120,13 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = 64 * WAVES_M, BN = 16 * TNW * WAVES_N;
   typedef Layout<BM, BN, NW> LY;
-  constexpr int LPW = (LY::a_panels + LY::b_panels) * 16 / NW;  // panel loads per wave
-  constexpr int LPS = LPW + 1;                                   // + one scale load
-  static_assert((LY::a_panels + LY::b_panels) * 16 == LPW * NW, "panel loads spread evenly");
+  constexpr int LPW = (LY::la + LY::lb) / NW;  // operand loads per wave
+  constexpr int LPS = LPW + 1;                  // + one scale load
+  static_assert(LY::la + LY::lb == LPW * NW, "operand loads spread evenly");
   static_assert(BM + BN <= 64 * NW, "at most one scale load per wave");
-  static_assert(TNW % 4 == 0, "the E8 form reads B fragments four at a time");
+  static_assert(BM % 64 == 0 && (BM <= 128 || BM % 128 == 0) && BN % 64 == 0 && (BN <= 128 || BN % 128 == 0),
+                "64-wide or whole 128-wide panels");
+  static_assert(TNW % 4 == 0 || TNW < 4, "the E8 form reads B fragments four at a time");
   static_assert(STAGES >= 2, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * LY::stage];
 
@@ -149,29 +168,38 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   const int kb0 = p.kb_start[g] + split * p.kb_per_split;
   const int nkb = S > 1 ? min(p.kb_per_split, p.kb_start[g + 1] - kb0) : p.kb_start[g + 1] - kb0;
 
-  // ---- direct-to-LDS load plan (the same per-lane offsets for every K block). Panel load
-  // u = LPW wave + i covers rows 8 (u % 16) + lane / 8 of panel u / 16 (A panels first),
-  // chunk position lane % 8, which holds logical chunk (lane % 8) ^ chunk_key(row).
+  // ---- direct-to-LDS load plan (the same per-lane offsets for every K block). Load
+  // u = LPW wave + i fills kilobyte u of the stage (A's loads first): load v of an operand
+  // covers, in a 128-wide K-major panel v / 16, K rows 8 (v % 16) + lane / 8 at chunk
+  // position lane % 8, which holds logical chunk (lane % 8) ^ chunk_key(k); in a 64-wide
+  // one, K rows 16 v + lane / 4 at position lane % 4 (logical chunk (lane % 4) ^
+  // chunk_key64(k)).
   uint32_t off[LPW];
   bool is_b[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int u = LPW * wave + i;
-    const int panel = u >> 4;
-    is_b[i] = panel >= LY::a_panels;
-    const int half = is_b[i] ? panel - LY::a_panels : panel;
+    is_b[i] = u >= LY::la;
+    const int v = is_b[i] ? u - LY::la : u;
     const int c0 = is_b[i] ? n0 : m0, lim = is_b[i] ? p.N : p.M;
     const uint32_t ld = (uint32_t)(is_b[i] ? p.ldb : p.lda);
     if (is_b[i] ? B_KC : A_KC) {
-      // K-contiguous: LDS row position 8 (u % 16) + lane / 8 holds tile row row_at(.),
-      // whose logical 16-byte K chunk (lane % 8) ^ (row & 7) sits at position lane % 8;
-      // rows past M / N re-read the tile's first row. Offset from the tile's first row.
-      const int row = 128 * half + row_at(8 * (u & 15) + (lane >> 3));
+      // K-contiguous: LDS row position 8 (v % 16) + lane / 8 of panel v / 16 holds tile
+      // row row_at(.), whose logical 16-byte K chunk (lane % 8) ^ (row & 7) sits at
+      // position lane % 8; rows past M / N re-read the tile's first row. Offset from the
+      // tile's first row.
+      const int row = 128 * (v >> 4) + row_at(8 * (v & 15) + (lane >> 3));
       const int c = (lane & 7) ^ (row & 7);
       off[i] = (c0 + row < lim ? (uint32_t)row : 0u) * ld + (uint32_t)(16 * c);
     } else {
-      const int k = 8 * (u & 15) + (lane >> 3);
-      const int col = 128 * half + 16 * ((lane & 7) ^ chunk_key(k));
+      int k, col;
+      if ((is_b[i] ? LY::wb : LY::wa) == 128) {
+        k = 8 * (v & 15) + (lane >> 3);
+        col = 128 * (v >> 4) + 16 * ((lane & 7) ^ chunk_key(k));
+      } else {
+        k = 16 * v + (lane >> 2);
+        col = 16 * ((lane & 3) ^ chunk_key64(k));
+      }
       const int col_g = c0 + col < lim ? c0 + col : c0;   // chunks past M / N re-read the first
       off[i] = (uint32_t)k * ld + (uint32_t)col_g;
     }
@@ -194,18 +222,32 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     const int64_t krow = (int64_t)(kb0 + kb) * kBlockK;
     const uint8_t* a_base = A_KC ? p.A + (int64_t)m0 * p.lda + krow : p.A + krow * p.lda;
     const uint8_t* b_base = B_KC ? p.B + (int64_t)n0 * p.ldb + krow : p.B + krow * p.ldb;
+    if (p.stream_b) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma16(is_b[i] ? b_base : a_base, off[i], st + (LPW * wave + i) * 1024);
+      for (int i = 0; i < LPW; ++i) {
+        if (is_b[i])
+          dma16nt(b_base, off[i], st + (LPW * wave + i) * 1024);
+        else
+          dma16(a_base, off[i], st + (LPW * wave + i) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma16(is_b[i] ? b_base : a_base, off[i], st + (LPW * wave + i) * 1024);
+    }
     dma4v(s_src + (int64_t)(kb0 + kb) * s_ld, st + LY::s_off + wave * 256);
   };
 
   // ---- fragment read plan: lane l = 16 q + i reads, for r = 0..3, K row 32 q + 8 r + i / 2,
   // the 8-byte half i & 1 of the fragment's chunk (chunk_key depends on the lane only)
   const int q = lane >> 4, li = lane & 15;
-  const int key = ((li >> 2) & 3) | ((q & 1) << 2);
+  // chunk_key / chunk_key64 of the lane's K rows (the same for its four reads)
+  const int key = ((li >> 2) & 3) | ((q & 1) << 2), key64 = ((li >> 3) & 1) | ((q & 1) << 1);
   const int rd_row = 32 * q + (li >> 1);                 // + 8 r
-  // byte offset of logical chunk c (16 columns) of an operand tile
-  auto frag_off = [&](int c) { return (c >> 3) * kPanel + rd_row * 128 + (((c & 7) ^ key) << 4) + 8 * (li & 1); };
+  // byte offset of logical chunk c (16 columns) of an operand tile of panel width W
+  auto frag_off = [&](int c, int W) {
+    return W == 128 ? (c >> 3) * kPanel + rd_row * 128 + (((c & 7) ^ key) << 4) + 8 * (li & 1)
+                    : rd_row * 64 + (((c & 3) ^ key64) << 4) + 8 * (li & 1);
+  };
   typedef __attribute__((address_space(3))) v2i_t* lds_v2i;
   // A fragment is read by RA (A) or RB (B) instructions: four transposing 8-byte reads
   // of a K-major operand, or two 16-byte reads of a K-contiguous one. Read r fills
@@ -213,18 +255,18 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
   constexpr int RA = A_KC ? 2 : 4, RB = B_KC ? 2 : 4;
   // K-contiguous operand: 16-row chunk c of the tile; lane 16 q + i takes row 16 c + i,
   // K bytes 32 q .. 32 q + 31 (logical 16-byte chunks 2q and 2q + 1)
-  auto read_part = [&](uint8_t* tile, int c, int r, bool kc, v8i& f) {
+  auto read_part = [&](uint8_t* tile, int c, int r, bool kc, int W, v8i& f) {
     if (kc) {
       const int row = 16 * (c & 7) + li;
       const uint4 v = *reinterpret_cast<const uint4*>(tile + (c >> 3) * kPanel + swz(row, 2 * q + r));
       f[4 * r] = (int)v.x, f[4 * r + 1] = (int)v.y, f[4 * r + 2] = (int)v.z, f[4 * r + 3] = (int)v.w;
     } else {
-      const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(v2i_t*)(tile + frag_off(c) + r * 8 * 128));
+      const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(v2i_t*)(tile + frag_off(c, W) + r * 8 * W));
       f[2 * r] = x[0], f[2 * r + 1] = x[1];
     }
   };
-  auto part_a = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st, c, r, A_KC, f); };
-  auto part_b = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st + LY::b_off, c, r, B_KC, f); };
+  auto part_a = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st, c, r, A_KC, LY::wa, f); };
+  auto part_b = [&](uint8_t* st, int c, int r, v8i& f) { read_part(st + LY::b_off, c, r, B_KC, LY::wb, f); };
 
   v4f acc[4][TNW];
 #pragma unroll
@@ -294,22 +336,23 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
         for (int r = 0; r < RA; ++r) part_a(st, 4 * wm + t, r, fa[t]);
         ea[t] = (__float_as_int(sa_t[t]) >> 23) & 0xFF;
       }
+      constexpr int GB = TNW < 4 ? TNW : 4;
 #pragma unroll
-      for (int jh = 0; jh < TNW / 4; ++jh) {
-        v8i fb[4];
-        int eb[4];
+      for (int jh = 0; jh < TNW / GB; ++jh) {
+        v8i fb[GB];
+        int eb[GB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < GB; ++j) {
 #pragma unroll
-          for (int r = 0; r < RB; ++r) part_b(st, cb0 + 4 * jh + j, r, fb[j]);
-          eb[j] = (__float_as_int(s_b[16 * (cb0 + 4 * jh + j) + li]) >> 23) & 0xFF;
+          for (int r = 0; r < RB; ++r) part_b(st, cb0 + GB * jh + j, r, fb[j]);
+          eb[j] = (__float_as_int(s_b[16 * (cb0 + GB * jh + j) + li]) >> 23) & 0xFF;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[t][4 * jh + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                fb[j], fa[t], acc[t][4 * jh + j], 0, 0, 0, eb[j], 0, ea[t]);
+          for (int j = 0; j < GB; ++j)
+            acc[t][GB * jh + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fb[j], fa[t], acc[t][GB * jh + j], 0, 0, 0, eb[j], 0, ea[t]);
       }
       continue;
     }
@@ -407,8 +450,8 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     // fragments of this wave whose rows start below M (the few-row shapes leave whole
     // fragments past M)
     const int live_t = max(0, min(4, (p.M - m0 - 64 * wm + 15) >> 4));
-    // (K is split only with 64x64 wave tiles: the reduce of a 64x128 one would spill)
-    if constexpr (TNW == 4) {
+    // (K is split only with 64x64 or 64x32 wave tiles: the reduce of a 64x128 one would spill)
+    if constexpr (TNW <= 4) {
       if (S > 1 && !reduce_splits(p.ws, p.counters, acc, tile, split, S, (wave * 4 * TNW) * 64 + lane, BM * BN, tid,
                                   &s_last, live_t))
         return;

@@ -258,9 +258,10 @@ def test_layout_argument_validation_without_launch(name, a_kc, b_kc):
 
 def test_layout_planner_splits_few_row_shapes():
     """The TN / NN / TT plan: 256x256 tiles when they give at least half the CUs a tile and
-    pad the output by at most a quarter, 128x128 otherwise; K split (at least two K blocks
-    a unit) when the 128x128 tiles leave more than half the CUs idle and the workspace holds
-    the partials; no split without a workspace."""
+    pad the output by at most a quarter; otherwise the 128x128, 64x128 or 128x64 tile and
+    the K split of least modelled time. K is split (at least five K blocks a unit, no
+    empty split) only as far as all units run in one round and the workspace holds the
+    partials; no split without a workspace."""
     fg.set_num_cus(256)
     try:
         L = fg.KIND_LAYOUT
@@ -270,25 +271,29 @@ def test_layout_planner_splits_few_row_shapes():
         mid = fg.query_config(L, 4096, 2112, 7168)     # 144 tiles of 256x256, N padded by 9%
         assert (mid["block_m"], mid["block_n"], mid["split_k"]) == (256, 256, 1)
         small = fg.query_config(L, 2048, 2048, 7168)   # 64 tiles of 256x256: 256 of 128x128
-        assert (small["block_m"], small["split_k"]) == (128, 1)
+        assert (small["block_m"], small["block_n"], small["split_k"]) == (128, 128, 1)
         wide = fg.query_config(L, 128, 32768, 512)     # 128 tiles of 256x256 would double the rows
         assert (wide["block_m"], wide["split_k"]) == (128, 1)
-        for M, N, K in [(64, 2112, 7168), (128, 7168, 2048), (128, 4096, 7168)]:
+        for M, N, K in [(64, 2112, 7168), (128, 7168, 2048), (128, 4096, 7168), (64, 7168, 16384)]:
             cfg = fg.query_config(L, M, N, K)
-            tiles = fg.num_tiles(M, N, 128, 128)
-            assert cfg["block_m"] == 128 and cfg["split_k"] > 1
+            bm, bn = cfg["block_m"], cfg["block_n"]
+            assert (bm, bn) in ((128, 128), (64, 128), (128, 64)) and cfg["split_k"] > 1
+            tiles = fg.num_tiles(M, N, bm, bn)
             assert cfg["num_units"] == tiles * cfg["split_k"] <= 256
             kbps = -(-(K // 128) // cfg["split_k"])
-            assert kbps >= 2 and -(-(K // 128) // kbps) == cfg["split_k"]   # no empty split
+            assert kbps >= 5 and -(-(K // 128) // kbps) == cfg["split_k"]   # no empty split
             ws = fg.workspace_size(L, M, N, K)
-            assert ws == 16384 + tiles * cfg["split_k"] * 128 * 128 * 4
+            assert ws == 16384 + tiles * cfg["split_k"] * bm * bn * 4
             assert fg.query_config(L, M, N, K, workspace_bytes=ws) == cfg
             assert fg.query_config(L, M, N, K, workspace_bytes=0)["split_k"] == 1
-        # a workspace too small for the chosen split falls back to a smaller one
+        # a workspace too small for the chosen split: another plan whose partials fit it
         M, N, K = 64, 2112, 7168
         cfg = fg.query_config(L, M, N, K)
-        small = fg.query_config(L, M, N, K, workspace_bytes=fg.workspace_size(L, M, N, K) // 2)
-        assert 1 < small["split_k"] < cfg["split_k"]
+        half = fg.workspace_size(L, M, N, K) // 2
+        small = fg.query_config(L, M, N, K, workspace_bytes=half)
+        assert small != cfg and small["split_k"] > 1
+        with fg.force_config(small["block_m"], small["block_n"], small["split_k"]):
+            assert fg.workspace_size(L, M, N, K) <= half
         with fg.force_config(256, 256, 3):
             f = fg.query_config(L, 64, 2112, 7168)
             assert (f["block_m"], f["split_k"]) == (256, 3)

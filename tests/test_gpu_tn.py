@@ -15,10 +15,11 @@ from parity_util import bits_of, compare, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["128x128", "128x128-2stage", "256x256"])
+@pytest.fixture(params=["128x128", "128x128-2stage", "256x256", "64x128", "128x64"])
 def tile(request):
-    """The three instances: 128x128 tiles with the 4-stage ring (a plan whose units all
-    fit one round), 128x128 with the 2-stage ring (more units than CUs) and 256x256."""
+    """The instances: 128x128 tiles with the 4-stage ring (a plan whose units all fit one
+    round), 128x128 with the 2-stage ring (more units than CUs), 256x256, and the 6-stage
+    64x128 and 128x64 tiles (64-wide panels of A, of B)."""
     if request.param == "128x128":
         fg.set_num_cus(1 << 20)
         yield request.param
@@ -27,7 +28,8 @@ def tile(request):
         if request.param == "256x256":
             yield request.param
         else:
-            with fg.force_config(128, 128, 1):
+            bm, bn = (128, 128) if request.param == "128x128-2stage" else (int(x) for x in request.param.split("x"))
+            with fg.force_config(bm, bn, 1):
                 yield request.param
     fg.set_num_cus(0)
 
@@ -230,6 +232,29 @@ def test_split_k_parity(cuda_device, layout, split, kind, M, N, K, ring):
 
 
 @pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+@pytest.mark.parametrize("split", [2, 3, 10])
+@pytest.mark.parametrize("kind", ["normal", "e1"])
+@pytest.mark.parametrize("M,N,K", [(65, 200, 1280), (300, 520, 1280)])
+@pytest.mark.parametrize("bm,bn", [(64, 128), (128, 64)])
+def test_split_k_parity_narrow_tiles(cuda_device, layout, split, kind, M, N, K, bm, bn):
+    """Split K on the 64x128 and 128x64 tiles (64-wide panels, 6-stage ring), twice through
+    one workspace."""
+    from parity_util import forced_workspace_bytes
+    c, At, Bt = tn_case(M, N, K, 5050 + split + M + bm, cuda_device, kind)
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
+    ws = torch.zeros(forced_workspace_bytes(fg.KIND_LAYOUT, M, N, K, 1, (bm, bn, split)), dtype=torch.uint8,
+                     device=cuda_device)
+    for rep in range(2):
+        D = c["D"].clone()
+        with fg.force_config(bm, bn, split):
+            fn(A, c["sa"], B, c["sb"], D, workspace=ws)
+        torch.cuda.synchronize()
+        compare(kind, bits_of(D), ref, f"{layout} {bm}x{bn} split {split} {kind} {M}x{N}x{K} call {rep}")
+    assert int(ws[:16384].view(torch.int32).abs().sum()) == 0   # every arrival counter reset
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
 def test_split_k_ue8m0_and_c(cuda_device, layout):
     from parity_util import forced_workspace_bytes
     M, N, K = 130, 260, 1536
@@ -256,7 +281,7 @@ def test_split_k_ue8m0_and_c(cuda_device, layout):
 
 
 def test_split_k_of_256_tiles_is_rejected(cuda_device):
-    """K is split only with 128x128 tiles (a 256x256 tile's reduce would spill)."""
+    """K is not split with 256x256 tiles (their reduce would spill)."""
     M, N, K = 64, 256, 1024
     c, At, Bt = tn_case(M, N, K, 5250, cuda_device, "e1")
     ws = torch.zeros(1 << 24, dtype=torch.uint8, device=cuda_device)
@@ -289,3 +314,21 @@ def test_planner_split_few_row_full_size(cuda_device, layout, M, N, K):
     torch.cuda.synchronize()
     ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
     compare("normal", bits_of(D), ref, f"{layout} {M}x{N}x{K} auto split {cfg['split_k']}")
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+def test_planner_256_tiles_ragged_n_full_size(cuda_device, layout):
+    """4096x2112x7168 with the planner's own plan on the full chip: 144 tiles of 256x256
+    (N = 8 tiles + 64 columns), checked on sampled rows, every column, against the oracle."""
+    M, N, K = 4096, 2112, 7168
+    cfg = fg.query_config(fg.KIND_LAYOUT, M, N, K)
+    assert (cfg["block_m"], cfg["block_n"], cfg["split_k"]) == (256, 256, 1)
+    c, At, Bt = tn_case(M, N, K, 5400, cuda_device, "normal")
+    A, B, fn = _layout_call(layout, c, At, Bt)
+    D = c["D"].clone()
+    fn(A, c["sa"], B, c["sb"], D)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24, 5401)
+    ref, _ = oracle.gemm_nt(c["A"].cpu().numpy()[rows], c["sa"].cpu().numpy()[:, rows], c["B"].cpu().numpy(),
+                            c["sb"].cpu().numpy())
+    compare("normal", bits_of(D)[rows], ref, f"{layout} {M}x{N}x{K} auto 256x256 sampled rows")
