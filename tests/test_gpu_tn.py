@@ -255,29 +255,30 @@ def test_split_k_parity_narrow_tiles(cuda_device, layout, split, kind, M, N, K, 
 
 
 @pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
-def test_split_k_ue8m0_and_c(cuda_device, layout):
+@pytest.mark.parametrize("bm,bn", [(128, 128), (64, 128), (128, 64)])
+def test_split_k_ue8m0_and_c(cuda_device, layout, bm, bn):
     from parity_util import forced_workspace_bytes
     M, N, K = 130, 260, 1536
-    ws = torch.zeros(forced_workspace_bytes(fg.KIND_LAYOUT, M, N, K, 1, (128, 128, 4)), dtype=torch.uint8,
+    ws = torch.zeros(forced_workspace_bytes(fg.KIND_LAYOUT, M, N, K, 1, (bm, bn, 4)), dtype=torch.uint8,
                      device=cuda_device)
     c, At, Bt = tn_case(M, N, K, 5100, cuda_device, "pow2")
     A, B, fn = _layout_call(layout, c, At, Bt)
     ref, _ = oracle.gemm_nt(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(), c["sb"].cpu().numpy())
     D = c["D"].clone()
-    with fg.force_config(128, 128, 4):
+    with fg.force_config(bm, bn, 4):
         fn(A, c["sa"], B, c["sb"], D, ue8m0=True, workspace=ws)
     torch.cuda.synchronize()
-    compare("normal", bits_of(D), ref, f"{layout} ue8m0 split 4")
+    compare("normal", bits_of(D), ref, f"{layout} {bm}x{bn} ue8m0 split 4")
     c, At, Bt = tn_case(M, N, K, 5101, cuda_device, "normal")
     A, B, fn = _layout_call(layout, c, At, Bt)
     C = (torch.randn(M, N, generator=synth.make_generator(5102, cuda_device), device=cuda_device) * 0.5).to(
         torch.bfloat16)
     ref, _ = oracle.gemm_nt_c(c["A"].cpu().numpy(), c["sa"].cpu().numpy(), c["B"].cpu().numpy(),
                               c["sb"].cpu().numpy(), bits_of(C))
-    with fg.force_config(128, 128, 4):
+    with fg.force_config(bm, bn, 4):
         fn(A, c["sa"], B, c["sb"], C, C=C, workspace=ws)      # in place: C is D
     torch.cuda.synchronize()
-    compare("normal", bits_of(C), ref, f"{layout} C in place split 4")
+    compare("normal", bits_of(C), ref, f"{layout} {bm}x{bn} C in place split 4")
 
 
 def test_split_k_of_256_tiles_is_rejected(cuda_device):
