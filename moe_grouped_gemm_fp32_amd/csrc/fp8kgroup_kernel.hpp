@@ -17,8 +17,8 @@
 //   panels (one [128 k][64 m] panel when BM = 64), the B tile likewise, and the block's
 //   BM + BN scales, filled by direct-to-LDS loads (16 bytes per lane, 8 lanes per 128-byte
 //   panel row, 4 per 64-byte row; one kilobyte per load instruction, spread evenly over
-//   the waves, and one scale load per wave per block). The
-//   FP8 MFMA wants each lane's 32 operand bytes to be 32 K values of one row, so the
+//   the waves, and one scale load per wave per block). The FP8 MFMA wants each lane's 32
+//   operand bytes to be 32 K values of one row, so the
 //   fragments are read with gfx950's transposing LDS read ds_read_b64_tr_b8: within each
 //   16-lane group, output lane i gets byte (i & 7) of the 8-byte rows addressed by lanes
 //   2j + (i >> 3), j = 0..7 (lane layout measured on the device). The lanes 2p and 2p+1
@@ -62,10 +62,10 @@ struct KParams {
   float* ws;
   int32_t* counters;
   int chunk;  // K-grouped: tiles per chunk (the CUs of one XCD), see the tile mapping
-  // dense layouts: 1 when one tile row covers all of M, so that each B tile is read by one
-  // unit: B is then loaded with the non-temporal hint (streamed past the caches, which
-  // keep A; measured on the few-row shapes: up to 22% faster, where B tiles are shared
-  // up to 18% slower)
+  // dense layouts (ignored by the K-grouped call): 1 when one tile row covers all of M, so
+  // that each B tile is read by one unit: B is then loaded with the non-temporal hint
+  // (streamed past the caches, which keep A; measured on the few-row shapes: up to 22%
+  // faster, where B tiles are shared up to 18% slower)
   int stream_b;
   int kb_start[kMaxKGroups + 1];  // group g covers K blocks [kb_start[g], kb_start[g+1])
 };
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1) fp8_k_grouped_tn_ke
     const int64_t krow = (int64_t)(kb0 + kb) * kBlockK;
     const uint8_t* a_base = A_KC ? p.A + (int64_t)m0 * p.lda + krow : p.A + krow * p.lda;
     const uint8_t* b_base = B_KC ? p.B + (int64_t)n0 * p.ldb + krow : p.B + krow * p.ldb;
-    if (p.stream_b) {
+    if (DENSE_TN && p.stream_b) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         if (is_b[i])
