@@ -93,15 +93,19 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-// Compiled variants: tile shape, wave layout (4 or 8 wave64s) and LDS ring depth.
-// Every variant uses 136-158 KB of LDS, so one workgroup runs per CU.
+// Compiled variants: tile shape, wave layout (4 or 8 wave64s) and LDS ring depth. One
+// workgroup runs per CU (the persistent grid has one per CU). Most rings fill the LDS;
+// the 64x64 and 128x96 tiles, which serve few-row calls whose units hold few K blocks,
+// keep 4 and 3 stages: with the full 8 and 5, each unit's first stage waits behind more
+// loads issued at once (measured on the six 64x64 and two 128x96 few-row shapes: 3-6%
+// faster with the shallower rings).
 struct Variant {
   int bm, bn, waves_m, waves_n, stages;
 };
 // The 96-column tiles (4 waves stacked along M) make 256 tiles of N=24576.
 constexpr Variant kVariants[] = {
-    {64, 64, 2, 2, 8},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},  {128, 128, 2, 2, 4},
-    {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}, {64, 96, 4, 1, 7},   {128, 96, 4, 1, 5}};
+    {64, 64, 2, 2, 4},  {128, 64, 2, 2, 6},  {64, 128, 2, 2, 6},  {128, 128, 2, 2, 4},
+    {256, 128, 4, 2, 3}, {128, 256, 2, 4, 3}, {64, 96, 4, 1, 7},   {128, 96, 4, 1, 3}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kOccupancy = 1;
 
