@@ -902,7 +902,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported" % args.gpus}))
+        print(json.dumps({"error": "the benchmark and the library run on one GPU; --gpus %d is not supported" % args.gpus}))
         sys.exit(2)
 
     if args.workload == "grouped":
